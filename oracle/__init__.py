@@ -1,0 +1,15 @@
+"""CPU oracle for the paged-KV attention path -- test infrastructure only.
+
+Imported only by the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; the product library never uses it.
+"""
+
+from .paged_kv import (  # noqa: F401
+    bf16_bits_to_float,
+    float_to_bf16_bits,
+    gather_kv,
+    paged_attention,
+    paged_decode,
+    store_kv,
+    token_slots,
+)
