@@ -1,0 +1,324 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  * Llama-3-8B attention geometry decode (32 q / 8 kv heads, head_dim 128,
+    page_size 16, 64 requests with lengths uniform in [512, 4096], pages
+    scattered in a pool of 32768): store_kv of the 64 new rows, then
+    split-KV decode and its merge;
+  * radix-shared prefix extend (same geometry, 16 requests sharing a
+    2048-token prefix, 512 new tokens each): store_kv of 8192 rows, then
+    causal extend.
+
+Reported: decode KV throughput in GB/s (the `value`, algorithmic bytes:
+K/V of every attended token, q, out, page ids and lengths; split partials
+not counted) and extend TFLOP/s (4*d FLOP per unmasked (query, key, head)),
+each against the MI355X peaks (HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s),
+with per-kernel times from HIP events on the launch stream, and the CPU
+oracle timed on a bounded sample of the same workloads.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def decode_bytes(wl, ph):
+    L = ph.seq_lens.astype(np.int64)
+    B = ph.batch
+    d, hkv, hq, ps = wl.head_dim, wl.num_kv_heads, wl.num_qo_heads, wl.page_size
+    return int((L * 2 * hkv * d * 2).sum() + 2 * B * hq * d * 2 + (-(-L // ps)).sum() * 4 + 8 * B)
+
+
+def store_bytes(wl, T):
+    return int(2 * (2 * T * wl.num_kv_heads * wl.head_dim * 2) + 4 * T)
+
+
+def extend_flops(wl, ph, rows=None):
+    d, hq = wl.head_dim, wl.num_qo_heads
+    tot = 0
+    cu = ph.cu_extend_lens
+    for r in range(ph.batch):
+        P = int(ph.prefix_lens[r])
+        for i in range(int(ph.extend_lens[r])):
+            if rows is None or (int(cu[r]) + i) in rows:
+                tot += (P + i + 1) * hq * 4 * d
+    return tot
+
+
+class Prepared:
+    """Device-resident inputs of one phase."""
+
+    def __init__(self, wl, ph, dev):
+        self.wl, self.ph = wl, ph
+        self.pool = wl.pool
+        self.pt = torch.from_numpy(wl.page_table).to(dev)
+        self.k, self.v, self.q = ph.k.to(dev), ph.v.to(dev), ph.q.to(dev)
+        self.loc = i32(ph.out_loc, dev)
+        self.ti = i32(ph.table_idx, dev)
+        self.sl = i32(ph.seq_lens, dev)
+        self.pl = i32(ph.prefix_lens, dev)
+        self.el = i32(ph.extend_lens, dev)
+        self.cu = i32(ph.cu_extend_lens, dev)
+        self.max_len = int(ph.seq_lens.max())
+        self.max_ext = int(ph.extend_lens.max())
+        self.out = torch.empty_like(self.q)
+        import paged_kv_attention_loc_amd as msgl
+        need = msgl.paged_decode_workspace_size(ph.batch, wl.num_qo_heads, wl.num_kv_heads,
+                                                wl.head_dim, self.max_len)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+
+def run_store(msgl, p):
+    msgl.store_kv(p.pool, p.wl.layer, p.k, p.v, p.loc)
+
+
+def run_decode(msgl, p):
+    msgl.paged_decode(p.pool, p.wl.layer, p.q, p.pt, p.ti, p.sl, p.max_len, out=p.out,
+                      workspace=p.ws)
+
+
+def run_extend(msgl, p):
+    msgl.paged_extend(p.pool, p.wl.layer, p.q, p.pt, p.ti, p.pl, p.el, p.cu, p.max_ext, p.max_len,
+                      out=p.out)
+
+
+def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
+    """The oracle, as it stands, on bounded samples of the same workloads."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    def bits(t):
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: copying pools to host ({cores} cores)")
+    pool_d = oracle.store_kv(bits(wl_dec.pool), 0, bits(ph_dec.k), bits(ph_dec.v), ph_dec.out_loc)
+    q_d = bits(ph_dec.q)
+    with threadpool_limits(limits=cores):
+        blas = [i.get("num_threads") for i in threadpool_info()]
+        # decode: requests in order, until half the budget is spent
+        t0 = time.perf_counter()
+        done = []
+        for r in range(ph_dec.batch):
+            sel = np.array([r])
+            oracle.paged_decode(pool_d, 0, q_d[sel], wl_dec.page_table, ph_dec.table_idx[sel],
+                                ph_dec.seq_lens[sel])
+            done.append(r)
+            if time.perf_counter() - t0 > budget_s / 2:
+                break
+        t_dec = time.perf_counter() - t0
+        L = ph_dec.seq_lens[done].astype(np.int64)
+        dec_b = int((L * 2 * wl_dec.num_kv_heads * wl_dec.head_dim * 2).sum()
+                    + 2 * len(done) * wl_dec.num_qo_heads * wl_dec.head_dim * 2
+                    + (-(-L // wl_dec.page_size)).sum() * 4 + 8 * len(done))
+        del pool_d
+        pool_e = oracle.store_kv(bits(wl_ext.pool), 0, bits(ph_ext.k), bits(ph_ext.v), ph_ext.out_loc)
+        q_e = bits(ph_ext.q)
+        rng = np.random.default_rng(0)
+        order = rng.permutation(ph_ext.num_tokens)
+        rows, t_ext, n = [], 0.0, 16
+        while t_ext < budget_s / 2 and len(rows) < ph_ext.num_tokens:
+            batch = [int(x) for x in order[len(rows): len(rows) + n]]
+            t1 = time.perf_counter()
+            oracle.paged_attention(pool_e, 0, q_e, wl_ext.page_table, ph_ext.table_idx,
+                                   ph_ext.prefix_lens, ph_ext.extend_lens, only_tokens=batch)
+            t_ext += time.perf_counter() - t1
+            rows += batch
+            n *= 2
+        ext_f = extend_flops(wl_ext, ph_ext, set(rows))
+    return {
+        "value": round(dec_b / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "blas_threads": blas,
+        "kind": "oracle",
+        "sample": (f"decode: {len(done)} of {ph_dec.batch} requests of the Llama-3-8B decode "
+                   f"batch ({int(L.sum())} KV tokens, {t_dec:.1f} s); extend: {len(rows)} of "
+                   f"{ph_ext.num_tokens} query rows of the radix-shared extend ({t_ext:.1f} s)"),
+        "extend_value": round(ext_f / t_ext / 1e9, 4),
+        "extend_unit": "GFLOP/s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle work")
+    ap.add_argument("--cold-iters", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(attention shards by heads/requests with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    import paged_kv_attention_loc_amd as msgl
+    from workloads import config_llama3_8b_decode, config_radix_shared_extend
+
+    msgl.load_library()
+    log("building workloads on the device")
+    wl_dec = config_llama3_8b_decode(device=dev)
+    wl_ext = config_radix_shared_extend(device=dev)
+    pd = Prepared(wl_dec, wl_dec.phases[0], dev)
+    pe = Prepared(wl_ext, wl_ext.phases[0], dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        run_store(msgl, pd)
+        if ev is not None:
+            ev[1].record()
+        run_decode(msgl, pd)
+        if ev is not None:
+            ev[2].record()
+        run_store(msgl, pe)
+        if ev is not None:
+            ev[3].record()
+        run_extend(msgl, pe)
+        if ev is not None:
+            ev[4].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)] for ev in events])  # ms
+    st_dec_ms, dec_ms, st_ext_ms, ext_ms = per.mean(axis=0)
+    dec_med = float(np.median(per[:, 1]))
+    ext_med = float(np.median(per[:, 3]))
+
+    # decode with the 256 MB MALL flushed before every launch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.cold_iters):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run_decode(msgl, pd)
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_ms = float(np.median(cold))
+
+    ph_d, ph_e = wl_dec.phases[0], wl_ext.phases[0]
+    dbytes = decode_bytes(wl_dec, ph_d)
+    eflops = extend_flops(wl_ext, ph_e)
+    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    ext_tflops = eflops / (ext_ms * 1e-3) / 1e12
+    sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
+    sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl_dec, ph_d, wl_ext, ph_e, args.cpu_budget)
+
+    result = {
+        "metric": "decode paged-attn KV GB/s + extend TFLOP/s on 1 MI355X (frac. of roofline)",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("llama3-8b-geometry decode: 32q/8kv d128 ps16 B64 L~U[512,4096] "
+                         "(sum L 154680) store_kv+decode; + radix-shared extend: 16 x "
+                         "(prefix 2048 shared + 512 new) store_kv+extend"),
+            "decode_batch": ph_d.batch,
+            "decode_sum_seq_len": int(ph_d.seq_lens.sum()),
+            "extend_batch": ph_e.batch,
+            "extend_tokens": ph_e.num_tokens,
+            "page_size": wl_dec.page_size,
+            "num_qo_heads": wl_dec.num_qo_heads,
+            "num_kv_heads": wl_dec.num_kv_heads,
+            "head_dim": wl_dec.head_dim,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "msgl_paged_decode (split-KV decode + merge)",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dbytes,
+            "avg_launch_us": round(dec_ms * 1e3, 3),
+            "median_launch_us": round(dec_med * 1e3, 3),
+            "cold_mall_median_us": round(cold_ms * 1e3, 3),
+            "cold_mall_GBs": round(dbytes / (cold_ms * 1e-3) / 1e9, 2),
+        },
+        "roofline_extend": {
+            "bound": "mfma",
+            "kernel": "msgl_paged_extend",
+            "achieved": round(ext_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": eflops,
+            "avg_launch_us": round(ext_ms * 1e3, 3),
+            "median_launch_us": round(ext_med * 1e3, 3),
+        },
+        "store_kv": {
+            "decode_rows": ph_d.num_tokens,
+            "decode_avg_us": round(st_dec_ms * 1e3, 3),
+            "decode_GBs": round(sb_dec / (st_dec_ms * 1e-3) / 1e9, 2),
+            "extend_rows": ph_e.num_tokens,
+            "extend_avg_us": round(st_ext_ms * 1e3, 3),
+            "extend_GBs": round(sb_ext / (st_ext_ms * 1e-3) / 1e9, 2),
+        },
+        "extend_tflops": round(ext_tflops, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * msgl.h -- C ABI of libmsgl.so: attention over a paged KV cache on MI355X
+ * (gfx950).
+ *
+ * The objects follow the Mini-SGLang pages:
+ *   - the KV pool is one bf16 tensor shaped
+ *     (2, num_layers, num_pages, page_size, num_kv_heads, head_dim), leading
+ *     index 0 = K, 1 = V ("Code Notes: mini-sglang", section "Engine Layer:
+ *     how to compute", table row BaseKVCachePool);
+ *   - store_kv writes new K/V rows into it "by out_loc indices" (same row);
+ *   - each request's KV is reached through one row of page_table, the row
+ *     picked by table_idx (same page, section "Scheduler Layer: what to
+ *     compute", table row TableManager);
+ *   - prefill/extend and decode are separate calls, as the HybridBackend
+ *     keeps separate prefill and decode backends (same page, Engine Layer
+ *     table, row BaseAttnBackend; "Code Structure", Attention Backends).
+ *
+ * Conventions shared by every call:
+ *   - A page_table entry is a page id in [0, num_pages).  Token p of a request
+ *     lives in slot page_table[row*page_table_stride + p / page_size] *
+ *     page_size + p % page_size of the (num_pages*page_size, num_kv_heads,
+ *     head_dim) view of one (K or V, layer).  out_loc entries are such slots.
+ *   - q head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *   - All pointers except the pool struct itself are device pointers.  The
+ *     caller owns every buffer; the library allocates no device memory and
+ *     keeps no state between calls other than a per-device architecture
+ *     check.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and performs no host synchronisation, so calls are
+ *     ordered by the stream: store_kv before the attention that reads it.
+ *   - Errors are returned, never thrown: scalar arguments are validated on
+ *     the host before any launch, and nothing is launched on error.  Device
+ *     contents (slots, page ids, table_idx, lengths) are the caller's
+ *     contract; with the environment variable MSGL_CHECK=1 each call copies
+ *     them to the host (a synchronisation) and returns MSGL_ERR_RANGE when
+ *     one is out of range, without launching.
+ *   - dtype is bf16 for pool, q, k, v and out; attention arithmetic is fp32.
+ *     head_dim must be 64 or 128, num_qo_heads a multiple of num_kv_heads
+ *     with a ratio of at most 16, page_size >= 1.  q/k/v/out/pool pointers
+ *     and row strides must be 16-byte aligned (strides a multiple of 8
+ *     elements) for the attention calls; store_kv accepts any alignment.
+ *   - Padding conventions for fixed-size batches: out_loc[t] < 0 skips row
+ *     t; seq_lens[r] == 0 in decode writes zeros and reads no KV.
+ */
+#ifndef MSGL_H
+#define MSGL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSGL_ABI_VERSION 1
+
+typedef int32_t msgl_status;
+#define MSGL_OK 0
+#define MSGL_ERR_NULL 1        /* a required pointer is NULL */
+#define MSGL_ERR_SHAPE 2       /* inconsistent sizes, strides or alignment */
+#define MSGL_ERR_UNSUPPORTED 3 /* head_dim, group size or device not supported */
+#define MSGL_ERR_WORKSPACE 4   /* decode workspace too small */
+#define MSGL_ERR_RANGE 5       /* checked mode: a device index/length out of range */
+#define MSGL_ERR_HIP 6         /* a HIP runtime call or launch failed */
+
+/* The KV pool: `data` is a device pointer to a contiguous bf16 tensor of
+ * shape (2, num_layers, num_pages, page_size, num_kv_heads, head_dim).
+ * The struct itself is read on the host during the call only. */
+typedef struct msgl_kv_pool {
+  void* data;
+  int32_t num_layers;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+} msgl_kv_pool;
+
+/* Version of this ABI (MSGL_ABI_VERSION). */
+int32_t msgl_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* msgl_status_string(msgl_status status);
+
+/*
+ * store_kv: for t < num_tokens with out_loc[t] >= 0, copy row t of k into
+ * K[layer] slot out_loc[t] and row t of v into V[layer] slot out_loc[t]
+ * ("Code Notes: mini-sglang", Engine Layer table, BaseKVCachePool row).
+ *   k, v        : (num_tokens, num_kv_heads, head_dim) bf16; heads and dims
+ *                 contiguous inside a row, rows `k_row_stride` /
+ *                 `v_row_stride` elements apart (>= num_kv_heads*head_dim),
+ *                 so slices of a merged QKV projection can be passed as is.
+ *   out_loc     : (num_tokens,) int32 slots in [0, num_pages*page_size), or
+ *                 negative for padding rows.  Slots must be distinct.
+ * A bit-exact copy: no value is converted.  num_tokens == 0 is a no-op.
+ */
+msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const int32_t* out_loc, int32_t num_tokens, void* stream);
+
+/*
+ * Bytes of workspace msgl_paged_decode needs for a batch with these sizes
+ * (fp32 split-KV partial outputs and their softmax statistics).  The value
+ * depends only on the arguments (and on MSGL_DECODE_SPLIT if set), so a
+ * workspace sized once for the largest batch and max_seq_len serves every
+ * smaller call.  Returns 0 for invalid sizes.
+ */
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_seq_len);
+
+/*
+ * paged_decode: one query token per request attends to all seq_lens[r]
+ * tokens of its KV (the new token's row already stored by store_kv), read
+ * through page_table row table_idx[r] ("Code Notes: mini-sglang", Engine
+ * Layer table rows BaseAttnBackend and GraphRunner -- decode batches of one
+ * new token per request; Scheduler Layer table, TableManager row).
+ *   out[r, h, :] = sum_j softmax_j(sm_scale * q[r,h,:] . K_j[h/G]) V_j[h/G]
+ *   q           : (batch, num_qo_heads, head_dim) bf16, rows q_row_stride
+ *                 elements apart.
+ *   out         : (batch, num_qo_heads, head_dim) bf16, contiguous.
+ *   page_table  : int32, row-major with page_table_stride entries per row;
+ *                 row table_idx[r] must hold >= ceil(seq_lens[r]/page_size)
+ *                 valid page ids (entries past that are never read).
+ *   table_idx   : (batch,) int32 row indices.
+ *   seq_lens    : (batch,) int32 in [0, max_seq_len]; 0 marks a padding row.
+ *   max_seq_len : host-side bound used to size the grid and the workspace.
+ *   sm_scale    : softmax scale, normally 1/sqrt(head_dim).
+ *   workspace   : device buffer of >= msgl_paged_decode_workspace_size(...)
+ *                 bytes; its contents need no initialisation.
+ * Long sequences are split into KV chunks processed in parallel and merged
+ * with a log-sum-exp combine.
+ */
+msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                              int64_t q_row_stride, void* out, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* table_idx,
+                              const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
+                              int32_t max_seq_len, float sm_scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * paged_extend: causal prefill/extend over a cached prefix.  Request r has
+ * prefix_lens[r] tokens already in the pool (a radix-cache hit or earlier
+ * prefill chunks) and extend_lens[r] new tokens, already stored, whose
+ * queries are rows cu_extend_lens[r] .. cu_extend_lens[r+1]-1 of q.  New
+ * token i sits at position prefix_lens[r] + i and attends to keys
+ * 0 .. prefix_lens[r] + i ("Code Notes: mini-sglang", Scheduler Layer table
+ * row PrefillManager -- chunked prefill; "Introduction", Key Features --
+ * Radix Cache and Chunked Prefill).  Rows of different requests may share
+ * page ids (shared prefixes).
+ *   q, out         : (total_extend_tokens, num_qo_heads, head_dim) bf16; q
+ *                    rows q_row_stride elements apart, out contiguous.
+ *   cu_extend_lens : (batch+1,) int32 exclusive prefix sum of extend_lens.
+ *   max_extend_len : host-side bound on extend_lens (sizes the grid).
+ *   max_seq_len    : host-side bound on prefix_lens + extend_lens.
+ * Requests with extend_lens[r] == 0 produce no rows.
+ */
+msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                              int64_t q_row_stride, void* out, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* table_idx,
+                              const int32_t* prefix_lens, const int32_t* extend_lens,
+                              const int32_t* cu_extend_lens, int32_t batch,
+                              int32_t total_extend_tokens, int32_t max_extend_len,
+                              int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                              void* stream);
+
+/*
+ * debug_gather_kv (for tests): copy tokens 0 .. len-1 of page_table row
+ * `row` out of the pool in logical order -- the page-table address
+ * translation the attention kernels use, exposed on its own.
+ *   k_out, v_out : (len, num_kv_heads, head_dim) bf16, contiguous.
+ */
+msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,
+                                 const int32_t* page_table, int32_t page_table_stride,
+                                 int32_t row, int32_t len, void* k_out, void* v_out,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSGL_H */

@@ -1,0 +1,236 @@
+"""Paged-KV attention for MI355X: Python binding of libmsgl.so.
+
+Argument marshalling only: every step of store_kv, decode and extend runs in
+the HIP kernels of ``libmsgl.so`` (see ``include/msgl.h`` for the contract).
+PyTorch supplies device memory and the current stream.  There is no CPU or
+PyTorch fallback: if the library is missing or the device is not gfx950,
+the calls raise.
+
+Objects follow the Mini-SGLang pages ("Code Notes: mini-sglang", Engine
+Layer table, BaseKVCachePool row; Scheduler Layer table, TableManager row):
+a bf16 pool shaped (2, num_layers, num_pages, page_size, kv_heads, head_dim),
+``out_loc`` slots for store_kv, and one ``page_table`` row per request
+picked by ``table_idx``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MsglError",
+    "library_path",
+    "load_library",
+    "abi_version",
+    "msgl_store_kv",
+    "msgl_paged_decode",
+    "msgl_paged_decode_workspace_size",
+    "msgl_paged_extend",
+    "msgl_debug_gather_kv",
+    "store_kv",
+    "paged_decode",
+    "paged_decode_workspace_size",
+    "paged_extend",
+    "debug_gather_kv",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmsgl.so"
+_lib = None
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_WORKSPACE",
+          5: "ERR_RANGE", 6: "ERR_HIP"}
+
+
+class MsglError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("num_layers", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("MSGL_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libmsgl.so (built in-tree by ``paged_kv_attention_loc_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_attention_loc_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    PP = ctypes.POINTER(_Pool)
+    lib.msgl_abi_version.restype = I32
+    lib.msgl_abi_version.argtypes = []
+    lib.msgl_status_string.restype = ctypes.c_char_p
+    lib.msgl_status_string.argtypes = [I32]
+    lib.msgl_store_kv.restype = I32
+    lib.msgl_store_kv.argtypes = [PP, I32, P, I64, P, I64, P, I32, P]
+    lib.msgl_paged_decode_workspace_size.restype = SZ
+    lib.msgl_paged_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.msgl_paged_decode.restype = I32
+    lib.msgl_paged_decode.argtypes = [PP, I32, P, I64, P, P, I32, P, P, I32, I32, I32, F32, P, SZ, P]
+    lib.msgl_paged_extend.restype = I32
+    lib.msgl_paged_extend.argtypes = [PP, I32, P, I64, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
+                                      F32, P]
+    lib.msgl_debug_gather_kv.restype = I32
+    lib.msgl_debug_gather_kv.argtypes = [PP, I32, P, I32, I32, I32, P, P, P]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().msgl_abi_version())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        text = load_library().msgl_status_string(status).decode()
+        raise MsglError(status, where, text)
+
+
+def _pool_struct(pool: torch.Tensor) -> _Pool:
+    if pool.dim() != 6 or pool.shape[0] != 2:
+        raise ValueError("pool must be shaped (2, num_layers, num_pages, page_size, kv_heads, head_dim)")
+    if pool.dtype != torch.bfloat16 or not pool.is_cuda or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous bf16 CUDA tensor")
+    _, nl, npg, ps, hkv, d = pool.shape
+    return _Pool(pool.data_ptr(), nl, npg, ps, hkv, d)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _rows(t: torch.Tensor, name: str, heads: int, d: int) -> int:
+    """Row stride of a (rows, heads, d) bf16 CUDA tensor with heads and dims packed."""
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise ValueError(f"{name} must be a bf16 CUDA tensor")
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != d:
+        raise ValueError(f"{name} must be shaped (rows, {heads}, {d}), got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError(f"{name}: heads and head_dim must be contiguous inside a row")
+    return int(t.stride(0)) if t.shape[0] > 1 else heads * d
+
+
+def _i32(t: torch.Tensor, name: str) -> int:
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+    return t.data_ptr()
+
+
+def msgl_store_kv(pool: torch.Tensor, layer: int, k: torch.Tensor, v: torch.Tensor,
+                  out_loc: torch.Tensor) -> None:
+    """Write row t of k / v into slot out_loc[t] of layer ``layer`` (negative = skip)."""
+    ps = _pool_struct(pool)
+    T = int(out_loc.numel())
+    ks = _rows(k, "k", ps.num_kv_heads, ps.head_dim)
+    vs = _rows(v, "v", ps.num_kv_heads, ps.head_dim)
+    if k.shape[0] != T or v.shape[0] != T:
+        raise ValueError("k, v and out_loc must have the same number of rows")
+    st = load_library().msgl_store_kv(ctypes.byref(ps), layer, k.data_ptr(), ks, v.data_ptr(), vs,
+                                      _i32(out_loc, "out_loc"), T, _stream(pool))
+    _check(st, "msgl_store_kv")
+
+
+def msgl_paged_decode_workspace_size(batch: int, num_qo_heads: int, num_kv_heads: int,
+                                     head_dim: int, max_seq_len: int) -> int:
+    return int(load_library().msgl_paged_decode_workspace_size(batch, num_qo_heads, num_kv_heads,
+                                                               head_dim, max_seq_len))
+
+
+def msgl_paged_decode(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
+                      table_idx: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention: q (B, Hq, d) -> out (B, Hq, d), reading each
+    request's seq_lens[r] tokens through page_table row table_idx[r]."""
+    ps = _pool_struct(pool)
+    B, hq, d = q.shape
+    qs = _rows(q, "q", hq, d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    need = msgl_paged_decode_workspace_size(B, hq, ps.num_kv_heads, d, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D (rows, entries)")
+    st = load_library().msgl_paged_decode(
+        ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
+        int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(seq_lens, "seq_lens"), B, hq,
+        int(max_seq_len), float(sm_scale), ws_ptr, ws_bytes, _stream(q))
+    _check(st, "msgl_paged_decode")
+    return out
+
+
+def msgl_paged_extend(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
+                      table_idx: torch.Tensor, prefix_lens: torch.Tensor, extend_lens: torch.Tensor,
+                      cu_extend_lens: torch.Tensor, max_extend_len: int, max_seq_len: int,
+                      sm_scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal extend attention: q (sum E, Hq, d) -> out (sum E, Hq, d)."""
+    ps = _pool_struct(pool)
+    T, hq, d = q.shape
+    qs = _rows(q, "q", hq, d)
+    B = int(table_idx.numel())
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.bfloat16, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D (rows, entries)")
+    st = load_library().msgl_paged_extend(
+        ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
+        int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(prefix_lens, "prefix_lens"),
+        _i32(extend_lens, "extend_lens"), _i32(cu_extend_lens, "cu_extend_lens"), B, T,
+        int(max_extend_len), int(max_seq_len), hq, float(sm_scale), _stream(q))
+    _check(st, "msgl_paged_extend")
+    return out
+
+
+def msgl_debug_gather_kv(pool: torch.Tensor, layer: int, page_table: torch.Tensor, row: int,
+                         length: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tokens 0 .. length-1 of page_table row ``row``, in logical order."""
+    ps = _pool_struct(pool)
+    k = torch.empty((length, ps.num_kv_heads, ps.head_dim), dtype=torch.bfloat16, device=pool.device)
+    v = torch.empty_like(k)
+    st = load_library().msgl_debug_gather_kv(ctypes.byref(ps), layer, _i32(page_table, "page_table"),
+                                             int(page_table.shape[1]), row, length, k.data_ptr(),
+                                             v.data_ptr(), _stream(pool))
+    _check(st, "msgl_debug_gather_kv")
+    return k, v
+
+
+# short names
+store_kv = msgl_store_kv
+paged_decode = msgl_paged_decode
+paged_decode_workspace_size = msgl_paged_decode_workspace_size
+paged_extend = msgl_paged_extend
+debug_gather_kv = msgl_debug_gather_kv

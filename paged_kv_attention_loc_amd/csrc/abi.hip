@@ -1,0 +1,370 @@
+// Host side of the C ABI declared in include/msgl.h: argument validation
+// (before any HIP call), the gfx950 check, the optional checked mode, and
+// the launch of the kernels on the caller's stream.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/msgl.h"
+#include "common.h"
+
+using namespace msgl;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+msgl_status hip_status(hipError_t e) { return e == hipSuccess ? MSGL_OK : MSGL_ERR_HIP; }
+
+// The kernels use gfx950 instructions (bf16 dot2, 32x32x16 bf16 MFMA).
+msgl_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MSGL_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MSGL_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MSGL_ERR_HIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MSGL_OK : MSGL_ERR_UNSUPPORTED;
+}
+
+msgl_status check_pool(const msgl_kv_pool* pool, int32_t layer) {
+  if (!pool || !pool->data) return MSGL_ERR_NULL;
+  if (pool->num_layers < 1 || pool->num_pages < 1 || pool->page_size < 1 ||
+      pool->num_kv_heads < 1 || pool->head_dim < 1)
+    return MSGL_ERR_SHAPE;
+  if (layer < 0 || layer >= pool->num_layers) return MSGL_ERR_SHAPE;
+  if (static_cast<int64_t>(pool->num_pages) * pool->page_size > INT32_MAX) return MSGL_ERR_SHAPE;
+  return MSGL_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t num_slots(const msgl_kv_pool* pool) {
+  return static_cast<int64_t>(pool->num_pages) * pool->page_size;
+}
+int64_t half_elems(const msgl_kv_pool* pool) {  // elements of one (K or V, layer)
+  return num_slots(pool) * pool->num_kv_heads * pool->head_dim;
+}
+const uint16_t* k_half(const msgl_kv_pool* pool, int32_t layer) {
+  return static_cast<const uint16_t*>(pool->data) + static_cast<int64_t>(layer) * half_elems(pool);
+}
+const uint16_t* v_half(const msgl_kv_pool* pool, int32_t layer) {
+  return static_cast<const uint16_t*>(pool->data) +
+         static_cast<int64_t>(pool->num_layers + layer) * half_elems(pool);
+}
+
+// Attention calls: geometry the kernels are built for.
+msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_heads) {
+  if (pool->head_dim != 64 && pool->head_dim != 128) return MSGL_ERR_UNSUPPORTED;
+  if (num_qo_heads < 1 || num_qo_heads % pool->num_kv_heads != 0) return MSGL_ERR_SHAPE;
+  if (num_qo_heads / pool->num_kv_heads > 16) return MSGL_ERR_UNSUPPORTED;
+  if (pool->num_kv_heads > 65535) return MSGL_ERR_UNSUPPORTED;
+  if (!aligned16(pool->data)) return MSGL_ERR_SHAPE;
+  return MSGL_OK;
+}
+
+// Tokens per decode split: a multiple of 64.  MSGL_DECODE_SPLIT overrides.
+int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t /*max_seq_len*/) {
+  const char* v = std::getenv("MSGL_DECODE_SPLIT");
+  if (v && v[0]) {
+    const long c = std::strtol(v, nullptr, 10);
+    if (c >= 64 && c <= (1 << 20)) return static_cast<int32_t>((c + 63) / 64 * 64);
+  }
+  return 256;
+}
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
+  dst.resize(n);
+  if (n == 0) return true;
+  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// Checked mode: the page ids that tokens 0 .. len-1 of a row would read.
+msgl_status check_row_pages(const int32_t* page_table, int64_t stride, int32_t row, int32_t len,
+                            const msgl_kv_pool* pool) {
+  if (row < 0) return MSGL_ERR_RANGE;
+  if (len <= 0) return MSGL_OK;
+  const int64_t npg = (len + pool->page_size - 1) / pool->page_size;
+  std::vector<int32_t> ids;
+  if (!copy_to_host(ids, page_table + static_cast<int64_t>(row) * stride, static_cast<size_t>(npg)))
+    return MSGL_ERR_HIP;
+  for (int32_t id : ids)
+    if (id < 0 || id >= pool->num_pages) return MSGL_ERR_RANGE;
+  return MSGL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msgl_abi_version(void) { return MSGL_ABI_VERSION; }
+
+const char* msgl_status_string(msgl_status s) {
+  switch (s) {
+    case MSGL_OK:
+      return "ok";
+    case MSGL_ERR_NULL:
+      return "a required pointer is NULL";
+    case MSGL_ERR_SHAPE:
+      return "inconsistent sizes, strides or alignment";
+    case MSGL_ERR_UNSUPPORTED:
+      return "unsupported head_dim, group size or device (gfx950 required)";
+    case MSGL_ERR_WORKSPACE:
+      return "decode workspace too small";
+    case MSGL_ERR_RANGE:
+      return "an index or length on the device is out of range (checked mode)";
+    case MSGL_ERR_HIP:
+      return "a HIP runtime call or kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const int32_t* out_loc, int32_t num_tokens, void* stream) {
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (num_tokens < 0) return MSGL_ERR_SHAPE;
+  if (num_tokens == 0) return MSGL_OK;
+  if (!k || !v || !out_loc) return MSGL_ERR_NULL;
+  const int64_t row = static_cast<int64_t>(pool->num_kv_heads) * pool->head_dim;
+  if (k_row_stride < row || v_row_stride < row) return MSGL_ERR_SHAPE;
+  const int row_bytes = static_cast<int>(row * 2);
+  // widest piece that keeps every row start and the pool aligned
+  int vec = 16;
+  auto fits = [&](int a) {
+    return (reinterpret_cast<uintptr_t>(k) % a) == 0 && (reinterpret_cast<uintptr_t>(v) % a) == 0 &&
+           ((k_row_stride * 2) % a) == 0 && ((v_row_stride * 2) % a) == 0 && (row_bytes % a) == 0 &&
+           (reinterpret_cast<uintptr_t>(pool->data) % a) == 0;
+  };
+  while (vec > 2 && !fits(vec)) vec >>= 1;
+  if (!fits(2)) return MSGL_ERR_SHAPE;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    std::vector<int32_t> loc;
+    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens))) return MSGL_ERR_HIP;
+    std::vector<int32_t> live;
+    for (int32_t s : loc) {
+      if (s >= num_slots(pool)) return MSGL_ERR_RANGE;
+      if (s >= 0) live.push_back(s);
+    }
+    std::vector<uint8_t> seen(static_cast<size_t>(num_slots(pool)), 0);
+    for (int32_t s : live) {
+      if (seen[s]) return MSGL_ERR_RANGE;
+      seen[s] = 1;
+    }
+  }
+  StoreParams p;
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.k_stride_bytes = k_row_stride * 2;
+  p.v_stride_bytes = v_row_stride * 2;
+  p.out_loc = out_loc;
+  p.k_cache = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(k_half(pool, layer)));
+  p.v_cache = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(v_half(pool, layer)));
+  p.pieces_per_row = row_bytes / vec;
+  p.row_bytes = row_bytes;
+  p.num_tokens = num_tokens;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.num_items = static_cast<int64_t>(num_tokens) * 2 * p.pieces_per_row;
+  return hip_status(launch_store_kv(p, vec, static_cast<hipStream_t>(stream)));
+}
+
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_seq_len) {
+  if (batch < 0 || num_qo_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 0)
+    return 0;
+  const int32_t chunk = decode_chunk(batch, num_kv_heads, max_seq_len);
+  const int64_t mc = (static_cast<int64_t>(max_seq_len) + chunk - 1) / chunk;
+  if (mc <= 1) return 0;
+  const int64_t units = static_cast<int64_t>(batch) * mc * num_qo_heads;
+  const int64_t o_bytes = units * head_dim * 4;
+  const int64_t ml_bytes = units * 2 * 4;
+  return static_cast<size_t>(((o_bytes + 255) / 256) * 256 + ml_bytes);
+}
+
+msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                              int64_t q_row_stride, void* out, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* table_idx,
+                              const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
+                              int32_t max_seq_len, float sm_scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (batch < 0 || max_seq_len < 0) return MSGL_ERR_SHAPE;
+  if (batch == 0) return MSGL_OK;
+  if (!q || !out || !page_table || !table_idx || !seq_lens) return MSGL_ERR_NULL;
+  st = check_attention_geometry(pool, num_qo_heads);
+  if (st != MSGL_OK) return st;
+  if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  const int32_t d = pool->head_dim;
+  if (q_row_stride < static_cast<int64_t>(num_qo_heads) * d || (q_row_stride % 8) != 0 ||
+      !aligned16(q) || !aligned16(out))
+    return MSGL_ERR_SHAPE;
+  if (page_table_stride < 1) return MSGL_ERR_SHAPE;
+  const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
+  if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
+  const size_t need =
+      msgl_paged_decode_workspace_size(batch, num_qo_heads, pool->num_kv_heads, d, max_seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSGL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MSGL_ERR_SHAPE;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    std::vector<int32_t> ti, sl;
+    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(sl, seq_lens, batch))
+      return MSGL_ERR_HIP;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (sl[b] < 0 || sl[b] > max_seq_len) return MSGL_ERR_RANGE;
+      st = check_row_pages(page_table, page_table_stride, ti[b], sl[b], pool);
+      if (st != MSGL_OK) return st;
+    }
+  }
+  DecodeParams p;
+  p.k_cache = k_half(pool, layer);
+  p.v_cache = v_half(pool, layer);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_stride = q_row_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.page_table = page_table;
+  p.pt_stride = page_table_stride;
+  p.table_idx = table_idx;
+  p.seq_lens = seq_lens;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.group = num_qo_heads / pool->num_kv_heads;
+  p.page_size = pool->page_size;
+  p.chunk = decode_chunk(batch, pool->num_kv_heads, max_seq_len);
+  p.max_chunks = static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + p.chunk - 1) / p.chunk);
+  if (p.max_chunks < 1) p.max_chunks = 1;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.max_seq_len = max_seq_len;
+  p.scale_log2 = sm_scale * kLog2e;
+  if (need > 0) {
+    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * num_qo_heads;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       ((units * d * 4 + 255) / 256) * 256);
+  } else {
+    p.ws_o = nullptr;
+    p.ws_ml = nullptr;
+  }
+  return hip_status(launch_decode(p, d, batch, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                              int64_t q_row_stride, void* out, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* table_idx,
+                              const int32_t* prefix_lens, const int32_t* extend_lens,
+                              const int32_t* cu_extend_lens, int32_t batch,
+                              int32_t total_extend_tokens, int32_t max_extend_len,
+                              int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                              void* stream) {
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (batch < 0 || total_extend_tokens < 0 || max_extend_len < 0 || max_seq_len < 0)
+    return MSGL_ERR_SHAPE;
+  if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return MSGL_OK;
+  if (!q || !out || !page_table || !table_idx || !prefix_lens || !extend_lens || !cu_extend_lens)
+    return MSGL_ERR_NULL;
+  st = check_attention_geometry(pool, num_qo_heads);
+  if (st != MSGL_OK) return st;
+  if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  const int32_t d = pool->head_dim;
+  if (q_row_stride < static_cast<int64_t>(num_qo_heads) * d || (q_row_stride % 8) != 0 ||
+      !aligned16(q) || !aligned16(out))
+    return MSGL_ERR_SHAPE;
+  if (max_extend_len > max_seq_len) return MSGL_ERR_SHAPE;
+  if (page_table_stride < 1) return MSGL_ERR_SHAPE;
+  const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
+  if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
+  const int32_t G = num_qo_heads / pool->num_kv_heads;
+  const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + 127) / 128;
+  if (mtiles > INT32_MAX) return MSGL_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    std::vector<int32_t> ti, pl, el, cu;
+    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(pl, prefix_lens, batch) ||
+        !copy_to_host(el, extend_lens, batch) || !copy_to_host(cu, cu_extend_lens, batch + 1))
+      return MSGL_ERR_HIP;
+    if (cu[0] != 0 || cu[batch] != total_extend_tokens) return MSGL_ERR_RANGE;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (pl[b] < 0 || el[b] < 0 || el[b] > max_extend_len ||
+          static_cast<int64_t>(pl[b]) + el[b] > max_seq_len || cu[b + 1] - cu[b] != el[b])
+        return MSGL_ERR_RANGE;
+      st = check_row_pages(page_table, page_table_stride, ti[b], pl[b] + el[b], pool);
+      if (st != MSGL_OK) return st;
+    }
+  }
+  ExtendParams p;
+  p.k_cache = k_half(pool, layer);
+  p.v_cache = v_half(pool, layer);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_stride = q_row_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.page_table = page_table;
+  p.pt_stride = page_table_stride;
+  p.table_idx = table_idx;
+  p.prefix_lens = prefix_lens;
+  p.extend_lens = extend_lens;
+  p.cu_extend = cu_extend_lens;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.group = G;
+  p.page_size = pool->page_size;
+  p.num_mtiles = static_cast<int32_t>(mtiles);
+  p.max_extend_len = max_extend_len;
+  p.max_seq_len = max_seq_len;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.scale_log2 = sm_scale * kLog2e;
+  return hip_status(launch_extend(p, d, batch, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,
+                                 const int32_t* page_table, int32_t page_table_stride,
+                                 int32_t row, int32_t len, void* k_out, void* v_out,
+                                 void* stream) {
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (len < 0 || row < 0 || page_table_stride < 1) return MSGL_ERR_SHAPE;
+  if (len == 0) return MSGL_OK;
+  if (!page_table || !k_out || !v_out) return MSGL_ERR_NULL;
+  if ((len + pool->page_size - 1) / pool->page_size > page_table_stride) return MSGL_ERR_SHAPE;
+  const int64_t row_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->head_dim * 2;
+  if ((row_bytes % 16) != 0 || !aligned16(k_out) || !aligned16(v_out) || !aligned16(pool->data))
+    return MSGL_ERR_SHAPE;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    st = check_row_pages(page_table, page_table_stride, row, len, pool);
+    if (st != MSGL_OK) return st;
+  }
+  GatherParams p;
+  p.k_cache = reinterpret_cast<const uint8_t*>(k_half(pool, layer));
+  p.v_cache = reinterpret_cast<const uint8_t*>(v_half(pool, layer));
+  p.page_row = page_table + static_cast<int64_t>(row) * page_table_stride;
+  p.k_out = static_cast<uint8_t*>(k_out);
+  p.v_out = static_cast<uint8_t*>(v_out);
+  p.row_bytes = static_cast<int32_t>(row_bytes);
+  p.pieces_per_row = static_cast<int32_t>(row_bytes / 16);
+  p.page_size = pool->page_size;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.num_items = static_cast<int64_t>(len) * 2 * p.pieces_per_row;
+  return hip_status(launch_gather(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

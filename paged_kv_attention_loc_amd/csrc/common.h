@@ -1,0 +1,191 @@
+// Device helpers and kernel parameter blocks shared by the HIP sources of
+// libmsgl.so.  gfx950 (CDNA4) only: wave64, bf16 dot2 and MFMA builtins.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msgl {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c, bf16 pairs in 32-bit words, fp32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// (a.lo16, b.lo16) and (a.hi16, b.hi16) as new bf16 pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------ wave64 reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Maximum over the 16 lanes of each DPP row, left in every lane of the row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  x += dpp_mov<kDppMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+// Wave-wide maximum / sum, returned uniformly.
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)),
+               fmaxf(lane_value(x, 32), lane_value(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+// --------------------------------------------------- page-table translation
+// Slot of logical token `tok` of the request whose page_table row is `row`:
+// page_table[row][tok / page_size] * page_size + tok % page_size.
+__device__ __forceinline__ int64_t token_slot(const int32_t* __restrict__ row, int tok,
+                                              int page_size) {
+  const int pg = tok / page_size;
+  return static_cast<int64_t>(row[pg]) * page_size + (tok - pg * page_size);
+}
+// The same, kept inside [0, num_slots): a page id outside the pool breaks
+// the caller's contract, and clamping turns it into wrong values instead of
+// an out-of-bounds access.
+__device__ __forceinline__ int token_slot_safe(const int32_t* __restrict__ row, int tok,
+                                               int page_size, int num_slots) {
+  const int pg = tok / page_size;
+  const int s = row[pg] * page_size + (tok - pg * page_size);
+  return min(max(s, 0), num_slots - 1);
+}
+
+// ------------------------------------------------------- parameter blocks
+struct StoreParams {
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t k_stride_bytes;
+  int64_t v_stride_bytes;
+  const int32_t* out_loc;
+  uint8_t* k_cache;  // K half of the layer, (slots, Hkv, d)
+  uint8_t* v_cache;
+  int64_t num_items;  // tokens * 2 * pieces_per_row
+  int32_t pieces_per_row;
+  int32_t row_bytes;
+  int32_t num_tokens;
+  int32_t num_slots;
+};
+
+struct GatherParams {
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* page_row;
+  uint8_t* k_out;
+  uint8_t* v_out;
+  int64_t num_items;
+  int32_t pieces_per_row;
+  int32_t row_bytes;
+  int32_t page_size;
+  int32_t num_slots;
+};
+
+struct DecodeParams {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const uint16_t* q;
+  int64_t q_stride;  // elements between consecutive requests' q rows
+  uint16_t* out;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* table_idx;
+  const int32_t* seq_lens;
+  float* ws_o;   // (batch, max_chunks, Hq, D) unnormalised partial outputs
+  float* ws_ml;  // (batch, max_chunks, Hq, 2) running max (log2 domain), sum
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t chunk;  // tokens per split, a multiple of 64
+  int32_t max_chunks;
+  int32_t max_seq_len;
+  int32_t num_slots;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct ExtendParams {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const uint16_t* q;
+  int64_t q_stride;
+  uint16_t* out;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* table_idx;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  const int32_t* cu_extend;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t num_mtiles;
+  int32_t max_extend_len;
+  int32_t max_seq_len;
+  int32_t num_slots;
+  float scale_log2;
+};
+
+// Launchers (defined next to their kernels); return the HIP status.
+hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStream_t stream);
+hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, hipStream_t stream);
+
+}  // namespace msgl

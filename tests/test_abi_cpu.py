@@ -1,0 +1,165 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No call here reaches a launch: every argument set is invalid in a way the
+host-side validation catches first (fake device addresses are never
+dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_loc_amd as msgl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msgl.h")
+
+OK, NULL, SHAPE, UNSUP, WS, RANGE, HIP = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _lib():
+    if not os.path.exists(msgl.library_path()):
+        pytest.fail("libmsgl.so is not built (run __graft_entry__.build())")
+    return msgl.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(msgl_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("msgl_store_kv", "msgl_paged_decode", "msgl_paged_extend",
+              "msgl_paged_decode_workspace_size", "msgl_status_string", "msgl_abi_version",
+              "msgl_debug_gather_kv"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.msgl_abi_version() == 1
+    for s in range(7):
+        assert lib.msgl_status_string(s)
+    assert lib.msgl_status_string(99) == b"unknown status"
+
+
+def _pool(**kw):
+    p = dict(data=FAKE, num_layers=2, num_pages=64, page_size=16, num_kv_heads=2, head_dim=128)
+    p.update(kw)
+    return msgl._Pool(p["data"], p["num_layers"], p["num_pages"], p["page_size"],
+                      p["num_kv_heads"], p["head_dim"])
+
+
+def test_workspace_size_is_host_arithmetic():
+    lib = _lib()
+    f = lib.msgl_paged_decode_workspace_size
+    assert f(64, 32, 8, 128, 256) == 0  # one split: no partials
+    n = f(64, 32, 8, 128, 4096)
+    chunks = 4096 // 256
+    units = 64 * chunks * 32
+    assert n == ((units * 128 * 4 + 255) // 256) * 256 + units * 8
+    assert f(-1, 32, 8, 128, 4096) == 0
+    # monotone in batch and length, so one allocation serves smaller calls
+    assert f(32, 32, 8, 128, 4096) <= n and f(64, 32, 8, 128, 2048) <= n
+
+
+def test_store_kv_rejects_bad_arguments_without_launch():
+    lib = _lib()
+    p = _pool()
+    f = lib.msgl_store_kv
+    assert f(None, 0, FAKE, 256, FAKE, 256, FAKE, 4, None) == NULL
+    assert f(ctypes.byref(_pool(data=0)), 0, FAKE, 256, FAKE, 256, FAKE, 4, None) == NULL
+    assert f(ctypes.byref(p), 2, FAKE, 256, FAKE, 256, FAKE, 4, None) == SHAPE  # layer
+    assert f(ctypes.byref(p), -1, FAKE, 256, FAKE, 256, FAKE, 4, None) == SHAPE
+    assert f(ctypes.byref(p), 0, None, 256, FAKE, 256, FAKE, 4, None) == NULL
+    assert f(ctypes.byref(p), 0, FAKE, 255, FAKE, 256, FAKE, 4, None) == SHAPE  # stride < row
+    assert f(ctypes.byref(p), 0, FAKE, 256, FAKE, 256, FAKE, -1, None) == SHAPE
+    assert f(ctypes.byref(p), 0, FAKE + 1, 256, FAKE, 256, FAKE, 4, None) == SHAPE  # odd address
+    assert f(ctypes.byref(p), 0, FAKE, 256, FAKE, 256, FAKE, 0, None) == OK  # empty: no-op
+    assert f(ctypes.byref(_pool(page_size=0)), 0, FAKE, 256, FAKE, 256, FAKE, 4, None) == SHAPE
+
+
+def _decode(lib, pool, **kw):
+    a = dict(layer=0, q=FAKE, q_stride=32 * 128, out=FAKE, pt=FAKE, pt_stride=256, ti=FAKE,
+             sl=FAKE, batch=4, hq=32, max_len=4096, scale=0.088, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.msgl_paged_decode(ctypes.byref(pool) if pool is not None else None, a["layer"],
+                                 a["q"], a["q_stride"], a["out"], a["pt"], a["pt_stride"],
+                                 a["ti"], a["sl"], a["batch"], a["hq"], a["max_len"], a["scale"],
+                                 a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_rejects_bad_arguments_without_launch():
+    lib = _lib()
+    p = _pool(num_kv_heads=8)
+    assert _decode(lib, None) == NULL
+    assert _decode(lib, p, q=None) == NULL
+    assert _decode(lib, p, sl=None) == NULL
+    assert _decode(lib, p, hq=30) == SHAPE  # not a multiple of kv heads
+    assert _decode(lib, p, hq=8 * 17) == UNSUP  # group above 16
+    assert _decode(lib, _pool(num_kv_heads=8, head_dim=96), q_stride=32 * 96) == UNSUP
+    assert _decode(lib, p, q_stride=32 * 128 - 8) == SHAPE
+    assert _decode(lib, p, q=FAKE + 8) == SHAPE  # misaligned
+    assert _decode(lib, p, pt_stride=255) == SHAPE  # rows too short for max_seq_len
+    assert _decode(lib, p, ws_bytes=16) == WS
+    assert _decode(lib, p, ws=None) == WS
+    assert _decode(lib, p, batch=-1) == SHAPE
+    assert _decode(lib, p, batch=0) == OK
+    assert _decode(lib, p, layer=5) == SHAPE
+
+
+def _extend(lib, pool, **kw):
+    a = dict(layer=0, q=FAKE, q_stride=32 * 128, out=FAKE, pt=FAKE, pt_stride=256, ti=FAKE,
+             pl=FAKE, el=FAKE, cu=FAKE, batch=2, total=100, max_ext=64, max_len=4096, hq=32,
+             scale=0.088)
+    a.update(kw)
+    return lib.msgl_paged_extend(ctypes.byref(pool) if pool is not None else None, a["layer"],
+                                 a["q"], a["q_stride"], a["out"], a["pt"], a["pt_stride"], a["ti"],
+                                 a["pl"], a["el"], a["cu"], a["batch"], a["total"], a["max_ext"],
+                                 a["max_len"], a["hq"], a["scale"], None)
+
+
+def test_extend_rejects_bad_arguments_without_launch():
+    lib = _lib()
+    p = _pool(num_kv_heads=8)
+    assert _extend(lib, None) == NULL
+    assert _extend(lib, p, cu=None) == NULL
+    assert _extend(lib, p, hq=33) == SHAPE
+    assert _extend(lib, _pool(num_kv_heads=8, head_dim=80), q_stride=32 * 80) == UNSUP
+    assert _extend(lib, p, max_ext=5000) == SHAPE  # extend longer than the sequence bound
+    assert _extend(lib, p, pt_stride=10) == SHAPE
+    assert _extend(lib, p, out=FAKE + 2) == SHAPE
+    assert _extend(lib, p, total=0) == OK
+    assert _extend(lib, p, batch=0) == OK
+
+
+def test_gather_rejects_bad_arguments_without_launch():
+    lib = _lib()
+    p = _pool()
+    f = lib.msgl_debug_gather_kv
+    assert f(ctypes.byref(p), 0, None, 16, 0, 10, FAKE, FAKE, None) == NULL
+    assert f(ctypes.byref(p), 0, FAKE, 16, -1, 10, FAKE, FAKE, None) == SHAPE
+    assert f(ctypes.byref(p), 0, FAKE, 1, 0, 40, FAKE, FAKE, None) == SHAPE  # row too short
+    assert f(ctypes.byref(p), 0, FAKE, 16, 0, 0, FAKE, FAKE, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("MSGL_LIBRARY", str(tmp_path / "missing.so"))
+    saved = msgl._lib
+    msgl._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            msgl.load_library()
+    finally:
+        msgl._lib = saved

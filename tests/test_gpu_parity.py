@@ -1,0 +1,418 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on gfx950.
+
+store_kv and the page-table gather must be bit-exact; attention outputs
+(bf16 in, fp32 accumulate, bf16 out) must satisfy, per element,
+|gpu - oracle| <= 1e-2 + 1e-2 * |oracle| (max-abs 1e-2 and max-rel 1e-2 in
+the combined form), with relative L2 <= 5e-3 as a tighter diagnostic that a
+wrong mask cannot hide under.
+
+Small cases are compared element by element in full; the full-size
+workloads are compared on sampled query rows that the oracle computes one
+by one (including the longest requests and the first/last rows of every
+chunk), in the same launch configuration the benchmark times.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_loc_amd as msgl
+from tests._util import bits, close_report, widen
+from workloads import CONFIG_BUILDERS, build_case
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-2
+REL_L2 = 5e-3
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    msgl.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+class Dev:
+    """Device copies of a workload's metadata and its current pool."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self.pool = wl.pool.cuda() if not wl.pool.is_cuda else wl.pool.clone()
+        self.pt = torch.from_numpy(wl.page_table).cuda()
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def gpu_phase(dev, ph, check_store_against=None):
+    wl = dev.wl
+    k, v, q = ph.k.cuda(), ph.v.cuda(), ph.q.cuda()
+    msgl.store_kv(dev.pool, wl.layer, k, v, _i32(ph.out_loc))
+    ti = _i32(ph.table_idx)
+    if ph.kind == "decode":
+        out = msgl.paged_decode(dev.pool, wl.layer, q, dev.pt, ti, _i32(ph.seq_lens),
+                                int(ph.seq_lens.max()))
+    else:
+        out = msgl.paged_extend(dev.pool, wl.layer, q, dev.pt, ti, _i32(ph.prefix_lens),
+                                _i32(ph.extend_lens), _i32(ph.cu_extend_lens),
+                                int(ph.extend_lens.max()), int(ph.seq_lens.max()))
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_phase(pool_bits, wl, ph, only_tokens=None):
+    pool_bits = oracle.store_kv(pool_bits, wl.layer, bits(ph.k), bits(ph.v), ph.out_loc)
+    if ph.kind == "decode":
+        ref = oracle.paged_decode(pool_bits, wl.layer, bits(ph.q), wl.page_table, ph.table_idx,
+                                  ph.seq_lens, only_tokens=only_tokens)
+    else:
+        ref = oracle.paged_attention(pool_bits, wl.layer, bits(ph.q), wl.page_table, ph.table_idx,
+                                     ph.prefix_lens, ph.extend_lens, only_tokens=only_tokens)
+    return pool_bits, ref
+
+
+def assert_close(got_bf16, ref, rows=None, what=""):
+    got = widen(bits(got_bf16), np.float64)
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    ok, max_abs, max_rel, rel_l2 = close_report(got, ref, ATOL, RTOL)
+    _say(f"{what}: max_abs={max_abs:.3e} max_rel={max_rel:.3e} rel_l2={rel_l2:.3e}")
+    assert ok, f"{what}: max_abs={max_abs} max_rel={max_rel}"
+    assert rel_l2 <= REL_L2, f"{what}: rel_l2={rel_l2}"
+
+
+def run_full(wl, what):
+    dev = Dev(wl)
+    pool_bits = bits(wl.pool)
+    for i, ph in enumerate(wl.phases):
+        _say(f"{what} phase {i} ({ph.kind}, B={ph.batch}, T={ph.num_tokens})")
+        out = gpu_phase(dev, ph)
+        pool_bits, ref = oracle_phase(pool_bits, wl, ph)
+        assert np.array_equal(bits(dev.pool), pool_bits), f"{what}: pool differs after store_kv"
+        assert_close(out, ref, what=f"{what} phase {i}")
+
+
+# ------------------------------------------------------------------ store/gather
+
+
+def test_store_kv_bit_exact_with_canaries():
+    wl = build_case(101, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                    prefix_lens=[3, 40, 0, 17], extend_lens=[5, 1, 70, 33])
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    _say("store_kv canaries")
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    torch.cuda.synchronize()
+    ref = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
+    assert np.array_equal(bits(dev.pool), ref)
+
+
+def test_store_kv_strided_views_and_padding():
+    # k and v as slices of a merged (T, Hq + 2 Hkv, d) projection; every
+    # third row padded with out_loc = -1
+    hq, hkv, d = 8, 2, 64
+    wl = build_case(102, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=4,
+                    prefix_lens=[0, 9], extend_lens=[30, 21])
+    ph = wl.phases[0]
+    T = ph.num_tokens
+    qkv = torch.zeros((T, hq + 2 * hkv, d), dtype=torch.bfloat16)
+    qkv[:, hq:hq + hkv] = ph.k
+    qkv[:, hq + hkv:] = ph.v
+    qkv = qkv.cuda()
+    loc = ph.out_loc.copy()
+    loc[::3] = -1
+    dev = Dev(wl)
+    _say("store_kv strided")
+    msgl.store_kv(dev.pool, 0, qkv[:, hq:hq + hkv], qkv[:, hq + hkv:], _i32(loc))
+    torch.cuda.synchronize()
+    ref = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), loc)
+    assert np.array_equal(bits(dev.pool), ref)
+
+
+@pytest.mark.parametrize("ps", [1, 2, 16, 64])
+def test_gather_bit_exact(ps):
+    wl = build_case(103 + ps, num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=ps,
+                    prefix_lens=[100, 7], extend_lens=[1, 90])
+    dev = Dev(wl)
+    ph = wl.phases[0]
+    for r in range(ph.batch):
+        L = int(ph.seq_lens[r])
+        row = int(ph.table_idx[r])
+        _say(f"gather ps={ps} row={row} L={L}")
+        k, v = msgl.debug_gather_kv(dev.pool, 0, dev.pt, row, L)
+        torch.cuda.synchronize()
+        kr, vr = oracle.gather_kv(bits(wl.pool), 0, wl.page_table, row, L)
+        assert np.array_equal(bits(k), kr) and np.array_equal(bits(v), vr)
+
+
+# --------------------------------------------------------------- the configs
+
+
+def test_tiny_config_full():
+    run_full(CONFIG_BUILDERS["tiny"](), "tiny")
+
+
+def _sampled(wl, ph, what, n_extra=6, seed=0):
+    """Run one phase at full size; compare sampled query rows."""
+    dev = Dev(wl)
+    pool_bits = bits(wl.pool)
+    rng = np.random.default_rng(seed)
+    out = gpu_phase(dev, ph)
+    if ph.kind == "decode":
+        L = ph.seq_lens
+        rows = set(int(x) for x in np.argsort(L)[-3:])  # the longest
+        rows |= set(int(x) for x in np.argsort(L)[:2])  # the shortest
+        rows |= set(int(x) for x in rng.choice(ph.batch, n_extra, replace=False))
+    else:
+        cu = ph.cu_extend_lens
+        rows = set()
+        for r in range(ph.batch):
+            if ph.extend_lens[r] > 0:
+                rows |= {int(cu[r]), int(cu[r + 1] - 1)}
+        rows |= set(int(x) for x in rng.choice(ph.num_tokens, n_extra, replace=False))
+    rows = sorted(rows)
+    pool_after = oracle.store_kv(pool_bits, wl.layer, bits(ph.k), bits(ph.v), ph.out_loc)
+    touched = np.unique(ph.out_loc[ph.out_loc >= 0])
+    S = wl.num_slots
+    gp = bits(dev.pool).reshape(2, S, -1)
+    op = pool_after.reshape(2, S, -1)
+    assert np.array_equal(gp[:, touched], op[:, touched]), f"{what}: stored rows differ"
+    probe = rng.choice(S, 4096, replace=False)
+    assert np.array_equal(gp[:, probe], op[:, probe]), f"{what}: untouched rows changed"
+    _, ref = oracle_phase(pool_bits, wl, ph, only_tokens=rows)
+    assert_close(out, ref, rows=rows, what=f"{what} ({len(rows)} sampled rows)")
+    return dev, pool_after
+
+
+def test_llama3_8b_decode_full_size():
+    wl = CONFIG_BUILDERS["llama3_8b_decode"](device="cuda")
+    _say("llama3_8b_decode full size")
+    _sampled(wl, wl.phases[0], "llama3_8b_decode")
+
+
+def test_qwen3_moe_decode_full_size():
+    wl = CONFIG_BUILDERS["qwen3_moe_decode"](device="cuda")
+    _say("qwen3_moe_decode full size")
+    _sampled(wl, wl.phases[0], "qwen3_moe_decode")
+
+
+def test_radix_shared_extend_full_size():
+    wl = CONFIG_BUILDERS["radix_shared_extend"](device="cuda")
+    _say("radix_shared_extend full size")
+    _sampled(wl, wl.phases[0], "radix_shared_extend", n_extra=10)
+
+
+def test_chunked_prefill_full_size():
+    wl = CONFIG_BUILDERS["chunked_prefill"](device="cuda")
+    dev = Dev(wl)
+    pool_bits = bits(wl.pool)
+    rng = np.random.default_rng(4)
+    for c, ph in enumerate(wl.phases):
+        _say(f"chunked_prefill chunk {c}")
+        out = gpu_phase(dev, ph)
+        E = ph.num_tokens
+        rows = sorted({0, 1, E // 2, E - 2, E - 1} | set(int(x) for x in rng.choice(E, 3, replace=False)))
+        pool_bits, ref = oracle_phase(pool_bits, wl, ph, only_tokens=rows)
+        assert_close(out, ref, rows=rows, what=f"chunked_prefill chunk {c}")
+
+
+# ------------------------------------------------------------------- sweeps
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("ps", [1, 16])
+def test_decode_sweep(d, G, ps):
+    hkv = 2
+    lens = [1, 2, 63, 64, 65, 255, 256, 257, 700, 1000]
+    wl = build_case(200 + d + G + ps, num_qo_heads=hkv * G, num_kv_heads=hkv, head_dim=d,
+                    page_size=ps, prefix_lens=[l - 1 for l in lens], extend_lens=[1] * len(lens),
+                    kind="decode")
+    run_full(wl, f"decode d={d} G={G} ps={ps}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("ps", [1, 16, 64])
+def test_extend_sweep(d, G, ps):
+    hkv = 2
+    P = [0, 5, 100, 17, 64, 0]
+    E = [1, 65, 33, 130, 16, 200]
+    wl = build_case(300 + d + G + ps, num_qo_heads=hkv * G, num_kv_heads=hkv, head_dim=d,
+                    page_size=ps, prefix_lens=P, extend_lens=E, kind="extend")
+    run_full(wl, f"extend d={d} G={G} ps={ps}")
+
+
+@pytest.mark.parametrize("E", [1, 2, 7, 31, 32, 33, 63, 64, 65])
+def test_extend_lengths(E):
+    wl = build_case(400 + E, num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16,
+                    prefix_lens=[37, 0], extend_lens=[E, E], kind="extend")
+    run_full(wl, f"extend E={E}")
+
+
+def test_extend_shared_prefix_small():
+    wl = build_case(411, num_qo_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                    prefix_lens=[128, 128, 128], extend_lens=[40, 129, 3], shared_prefix=True,
+                    kind="extend")
+    run_full(wl, "extend shared prefix")
+
+
+def test_extend_with_empty_request():
+    wl = build_case(412, num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                    prefix_lens=[20, 50, 3], extend_lens=[10, 0, 5], kind="extend")
+    run_full(wl, "extend with an empty request")
+
+
+# --------------------------------------------------------------- exact cases
+
+
+def test_single_key_is_exact():
+    for kind in ("decode", "extend"):
+        wl = build_case(501, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                        prefix_lens=[0, 0], extend_lens=[1, 1], kind=kind)
+        dev = Dev(wl)
+        ph = wl.phases[0]
+        _say(f"single key {kind}")
+        out = gpu_phase(dev, ph)
+        expect = np.repeat(bits(ph.v), 4, axis=1)  # q head h reads kv head h // 4
+        assert np.array_equal(bits(out), expect)
+
+
+def test_boundary_probes_gpu():
+    # query row i probes channel i; key a+1 (first masked) or key a (last
+    # allowed) carries a huge logit on that channel
+    d, hq, hkv, ps = 128, 4, 1, 16
+    P, E = 45, 40
+    L = P + E
+    base = build_case(502, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                      prefix_lens=[P], extend_lens=[E], kind="extend")
+    ph = base.phases[0]
+    q = torch.zeros_like(ph.q)
+    for i in range(E):
+        q[i, :, i] = 64.0
+    for mode in ("leak", "mirror"):
+        K = torch.zeros((L, hkv, d), dtype=torch.bfloat16)
+        for i in range(E):
+            a = P + i
+            if mode == "leak" and a + 1 < L:
+                K[a + 1, :, i] = 64.0
+            if mode == "mirror":
+                K[a, :, i] = 64.0
+        # write all L rows (prefix and new) through store_kv
+        pool = base.pool.clone()
+        slots = oracle.token_slots(base.page_table[ph.table_idx[0]], L, ps)
+        Vall = torch.randn((L, hkv, d), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+        dev = Dev(base)
+        msgl.store_kv(dev.pool, 0, K.cuda(), Vall.cuda(), _i32(slots))
+        _say(f"boundary probe {mode}")
+        out = msgl.paged_extend(dev.pool, 0, q.cuda(), dev.pt, _i32(ph.table_idx), _i32([P]),
+                                _i32([E]), _i32([0, E]), E, L)
+        torch.cuda.synchronize()
+        got = widen(bits(out), np.float64)
+        Vw = widen(bits(Vall), np.float64)
+        for i in range(E):
+            a = P + i
+            if mode == "leak":
+                expect = Vw[: a + 1, 0].mean(axis=0)
+                assert np.abs(got[i] - expect[None]).max() <= 2e-2, f"mask leak at row {i}"
+            else:
+                assert np.array_equal(bits(out)[i], np.repeat(bits(Vall)[a:a + 1, 0], hq, 0))
+
+
+def test_decode_matches_extend_of_one():
+    wl = build_case(503, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    prefix_lens=[99, 700, 2047, 1], extend_lens=[1, 1, 1, 1], kind="decode")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    _say("decode vs extend(E=1)")
+    dec = gpu_phase(dev, ph)
+    ext = msgl.paged_extend(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
+                            _i32(ph.prefix_lens), _i32(ph.extend_lens), _i32(ph.cu_extend_lens),
+                            1, int(ph.seq_lens.max()))
+    torch.cuda.synchronize()
+    ok, max_abs, _, rel = close_report(widen(bits(dec)), widen(bits(ext)))
+    assert ok and rel <= REL_L2, (max_abs, rel)
+
+
+def test_decode_padding_rows_are_zero():
+    wl = build_case(504, num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                    prefix_lens=[30, 400, 5], extend_lens=[1, 1, 1], kind="decode")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    L = ph.seq_lens.copy()
+    L[1] = 0
+    _say("decode padding row")
+    out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx), _i32(L), 512)
+    torch.cuda.synchronize()
+    pool_bits = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
+    ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, L)
+    assert np.all(bits(out)[1] == 0)
+    assert_close(out, ref, rows=[0, 2], what="decode with a padding row")
+
+
+def test_decode_workspace_reuse_and_split_override(monkeypatch):
+    # a workspace sized for the largest call serves smaller ones; the split
+    # size override changes the partition but not the result
+    wl = build_case(505, num_qo_heads=16, num_kv_heads=2, head_dim=128, page_size=16,
+                    prefix_lens=[1500, 37, 900], extend_lens=[1, 1, 1], kind="decode")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    pool_bits = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
+    ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, ph.seq_lens)
+    need = msgl.paged_decode_workspace_size(64, 16, 2, 128, 8192)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for split in ("64", "256", "1024"):
+        monkeypatch.setenv("MSGL_DECODE_SPLIT", split)
+        _say(f"decode split {split}")
+        out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
+                                _i32(ph.seq_lens), 2048, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out, ref, what=f"decode split {split}")
+
+
+# -------------------------------------------------------------- checked mode
+
+
+def test_checked_mode_rejects_bad_device_metadata(monkeypatch):
+    monkeypatch.setenv("MSGL_CHECK", "1")
+    wl = build_case(506, num_qo_heads=4, num_kv_heads=1, head_dim=64, page_size=16,
+                    prefix_lens=[10, 20], extend_lens=[1, 1], kind="decode")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    k, v = ph.k.cuda(), ph.v.cuda()
+    dup = ph.out_loc.copy()
+    dup[1] = dup[0]
+    with pytest.raises(msgl.MsglError) as e:
+        msgl.store_kv(dev.pool, 0, k, v, _i32(dup))
+    assert e.value.status == 5
+    far = ph.out_loc.copy()
+    far[0] = wl.num_slots
+    with pytest.raises(msgl.MsglError):
+        msgl.store_kv(dev.pool, 0, k, v, _i32(far))
+    bad_pt = wl.page_table.copy()
+    bad_pt[ph.table_idx[0], 0] = wl.num_pages + 5
+    with pytest.raises(msgl.MsglError):
+        msgl.paged_decode(dev.pool, 0, ph.q.cuda(), torch.from_numpy(bad_pt).cuda(),
+                          _i32(ph.table_idx), _i32(ph.seq_lens), 32)
+    with pytest.raises(msgl.MsglError):  # seq_len above max_seq_len
+        msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx), _i32(ph.seq_lens), 16)
+    # the valid call still runs in checked mode
+    msgl.store_kv(dev.pool, 0, k, v, _i32(ph.out_loc))
+    out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
+                            _i32(ph.seq_lens), 32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
