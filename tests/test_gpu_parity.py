@@ -355,7 +355,7 @@ def test_decode_padding_rows_are_zero():
     L = ph.seq_lens.copy()
     L[1] = 0
     _say("decode padding row")
-    out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx), _i32(L), 512)
+    out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx), _i32(L), 401)
     torch.cuda.synchronize()
     pool_bits = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
     ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, L)
@@ -379,7 +379,7 @@ def test_decode_workspace_reuse_and_split_override(monkeypatch):
         monkeypatch.setenv("MSGL_DECODE_SPLIT", split)
         _say(f"decode split {split}")
         out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
-                                _i32(ph.seq_lens), 2048, workspace=ws)
+                                _i32(ph.seq_lens), int(ph.seq_lens.max()), workspace=ws)
         torch.cuda.synchronize()
         assert_close(out, ref, what=f"decode split {split}")
 
