@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle work")
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -240,6 +242,16 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
     cold_ms = float(np.median(cold))
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 512 MiB device copies")
+        del src, dst
 
     ph_d, ph_e = wl_dec.phases[0], wl_ext.phases[0]
     dbytes = decode_bytes(wl_dec, ph_d)
