@@ -90,7 +90,7 @@ class Prepared:
         import paged_kv_attention_loc_amd as msgl
         need = msgl.paged_decode_workspace_size(ph.batch, wl.num_qo_heads, wl.num_kv_heads,
                                                 wl.head_dim, self.max_len)
-        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
 
 
 def run_store(msgl, p):

@@ -99,7 +99,8 @@ msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k
 
 /*
  * Bytes of workspace msgl_paged_decode needs for a batch with these sizes
- * (fp32 split-KV partial outputs and their softmax statistics).  The value
+ * (fp32 split-KV partial outputs and their softmax statistics); 0 when no
+ * request can need more than one split.  The value
  * depends only on the arguments (and on MSGL_DECODE_SPLIT if set), so a
  * workspace sized once for the largest batch and max_seq_len serves every
  * smaller call.  Returns 0 for invalid sizes.
@@ -126,9 +127,12 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
  *   max_seq_len : host-side bound used to size the grid and the workspace.
  *   sm_scale    : softmax scale, normally 1/sqrt(head_dim).
  *   workspace   : device buffer of >= msgl_paged_decode_workspace_size(...)
- *                 bytes; its contents need no initialisation.
- * Long sequences are split into KV chunks processed in parallel and merged
- * with a log-sum-exp combine.
+ *                 bytes; its contents need no initialisation.  Calls that
+ *                 share a workspace must not overlap in time (same stream,
+ *                 or synchronised).
+ * Long sequences are split into KV chunks processed in parallel; a second
+ * kernel on the same stream merges the partial results with a log-sum-exp
+ * combine.
  */
 msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const void* q,
                               int64_t q_row_stride, void* out, const int32_t* page_table,

@@ -154,6 +154,7 @@ def msgl_store_kv(pool: torch.Tensor, layer: int, k: torch.Tensor, v: torch.Tens
 
 def msgl_paged_decode_workspace_size(batch: int, num_qo_heads: int, num_kv_heads: int,
                                      head_dim: int, max_seq_len: int) -> int:
+    """Bytes of decode workspace (fp32 split partials); 0 if none is needed."""
     return int(load_library().msgl_paged_decode_workspace_size(batch, num_qo_heads, num_kv_heads,
                                                                head_dim, max_seq_len))
 

@@ -6,7 +6,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/msgl.h"
+#include "msgl.h"
 #include "common.h"
 
 using namespace msgl;
@@ -74,14 +74,24 @@ msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_he
   return MSGL_OK;
 }
 
-// Tokens per decode split: a multiple of 64.  MSGL_DECODE_SPLIT overrides.
-int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t /*max_seq_len*/) {
+// Decode workspace layout: fp32 partial outputs (batch, max_chunks, Hq, d),
+// then their (max, sum) pairs, 256-byte aligned.
+// Tokens per decode split: a multiple of 64 (MSGL_DECODE_SPLIT overrides
+// the default of 64 -- short splits keep many independent waves in flight,
+// which measured faster than longer ones despite the extra partials),
+// doubled until no request can need more than
+// kMaxDecodeSplits splits -- the merge kernel keeps one weight per split in
+// LDS.
+constexpr int64_t kMaxDecodeSplits = 4096;
+int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_seq_len) {
+  int64_t c = 64;
   const char* v = std::getenv("MSGL_DECODE_SPLIT");
   if (v && v[0]) {
-    const long c = std::strtol(v, nullptr, 10);
-    if (c >= 64 && c <= (1 << 20)) return static_cast<int32_t>((c + 63) / 64 * 64);
+    const long e = std::strtol(v, nullptr, 10);
+    if (e >= 64 && e <= (1 << 20)) c = (e + 63) / 64 * 64;
   }
-  return 256;
+  while ((static_cast<int64_t>(max_seq_len) + c - 1) / c > kMaxDecodeSplits) c *= 2;
+  return static_cast<int32_t>(c);
 }
 
 template <typename T>
@@ -212,6 +222,8 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   st = check_attention_geometry(pool, num_qo_heads);
   if (st != MSGL_OK) return st;
   if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  // decode addresses one (K or V, layer) sub-tensor with 32-bit byte offsets
+  if (half_elems(pool) * 2 >= (int64_t{1} << 32)) return MSGL_ERR_UNSUPPORTED;
   const int32_t d = pool->head_dim;
   if (q_row_stride < static_cast<int64_t>(num_qo_heads) * d || (q_row_stride % 8) != 0 ||
       !aligned16(q) || !aligned16(out))
@@ -252,13 +264,17 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   p.max_chunks = static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + p.chunk - 1) / p.chunk);
   if (p.max_chunks < 1) p.max_chunks = 1;
   p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
+  p.page_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if (pool->page_size == (1 << b)) p.page_shift = b;
   p.max_seq_len = max_seq_len;
   p.scale_log2 = sm_scale * kLog2e;
   if (need > 0) {
     const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * num_qo_heads;
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                       ((units * d * 4 + 255) / 256) * 256);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_ml = reinterpret_cast<float*>(ws + ((units * d * 4 + 255) / 256) * 256);
   } else {
     p.ws_o = nullptr;
     p.ws_ml = nullptr;

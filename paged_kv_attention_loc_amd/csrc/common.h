@@ -153,10 +153,12 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t group;
   int32_t page_size;
+  int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
   int32_t chunk;  // tokens per split, a multiple of 64
   int32_t max_chunks;
   int32_t max_seq_len;
   int32_t num_slots;
+  uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
   float scale_log2;  // sm_scale * log2(e)
 };
 

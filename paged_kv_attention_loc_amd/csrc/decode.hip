@@ -4,36 +4,71 @@
 // through the request's page_table row ("Code Notes: mini-sglang", Engine
 // Layer table rows BaseAttnBackend / GraphRunner; Scheduler Layer table row
 // TableManager).  The work is HBM-bound: every K/V byte is read once and
-// used for G = q_heads / kv_heads query heads, so the kernel is built around
-// streaming K/V with wide loads, not around matrix cores.
+// used for G = q_heads / kv_heads query heads, so the kernel is built to
+// keep many waves -- and so many loads -- in flight per CU, with no matrix
+// cores involved.
 //
-// One wave64 workgroup handles (request, kv head, chunk of `chunk` tokens),
-// in tiles of 64 tokens:
-//   * each lane owns one token of the tile for q.K: the tile's K rows are
-//     staged in LDS (16-byte pieces, XOR-swizzled by token so that the
-//     token-per-lane reads are bank-conflict free) and every lane runs
-//     v_dot2_f32_bf16 over its own row against the G query heads, which are
-//     broadcast from LDS;
+// One wave64 workgroup handles (request, kv head, chunk of `chunk` tokens)
+// in tiles of 32 tokens.  A wave needs about 9-11 KiB of LDS and few
+// registers, so a CU holds 16 of them and their loads overlap each other's
+// arithmetic; chunks are short (64 tokens by default) so that many
+// independent waves are in flight -- measured faster than fewer, longer
+// waves despite the extra partials.
+//   * addressing: one vector load per tile fetches the tile's page ids
+//     (lane t: token t), one tile ahead; each token's row byte offset is
+//     then moved into an SGPR (v_readlane) and every K/V load is a buffer
+//     load of that whole token row (4 bytes per lane, one row per
+//     instruction).  No lane holds a 64-bit address, and an offset past
+//     the pool reads zeros instead of faulting;
+//   * q.K: two neighbouring lanes own one token (half of the channels
+//     each).  K rows pass through LDS with one 16-byte piece of padding per
+//     row (conflict-free reads, addresses base + immediate), q is broadcast
+//     from LDS one head at a time, v_dot2_f32_bf16 does the products and one
+//     DPP add joins the halves;
 //   * softmax statistics are kept per head in the log2 domain (scale folded
-//     into the exponent), the tile maximum via DPP row reductions;
-//   * for p.V each lane owns 8 channels of every 4th (d = 128) or 8th
-//     (d = 64) token, with V loaded straight into registers by coalesced
-//     16-byte loads; two tokens' V values are paired with v_perm and
-//     multiplied by the matching bf16 pair of probabilities with one
-//     v_dot2_f32_bf16;
-//   * a request with a single chunk writes its bf16 output directly, longer
-//     ones write fp32 partials (unnormalised o, max, sum) for the merge.
+//     into the exponent); the tile maximum comes from DPP row reductions;
+//   * p.V: each lane owns two channels of every token and keeps its V words
+//     in registers; two tokens' values are paired with v_perm and weighted
+//     by the matching bf16 pair of probabilities (an LDS broadcast) in one
+//     v_dot2_f32_bf16: two accumulators per head;
+//   * a request with a single chunk writes its bf16 output directly; longer
+//     ones write fp32 partials (unnormalised o, max, sum) that the merge
+//     kernel combines.
 #include "common.h"
 
 namespace msgl {
 
+namespace {
+
+template <int D>
+struct DecodeShape {
+  static constexpr int TILE = 32;     // tokens per tile
+  static constexpr int LPT = D / 8;   // 16-byte pieces per token row
+  static constexpr int HPC = LPT / 2; // pieces per q.K half-row
+  static constexpr int CPL = D / 2;   // 4-byte words per token row
+  // LDS row pitch of K in words: one 16-byte piece of padding per row
+  static constexpr int KROW = CPL + 4;
+};
+
+// Waves per SIMD the register allocation must leave room for: occupancy is
+// what hides the HBM latency here.
+template <int GM>
+struct DecodeOccupancy {
+  static constexpr int value = GM <= 8 ? 4 : 2;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  // dword 3 = 0x00020000: 32-bit data format, raw (unswizzled) addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+}  // namespace
+
 template <int D, int GM>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
-  constexpr int LPT = D / 8;     // lanes per 16-byte-piece token row
-  constexpr int TPI = 64 / LPT;  // tokens per wave-wide load
-  constexpr int NI = 64 / TPI;   // loads per 64-token tile
-  constexpr int TILE = 64;
-  static_assert(NI % 2 == 0, "token pairs");
+__global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_kernel(
+    DecodeParams p, const int32_t* __restrict__ page_table) {
+  using S = DecodeShape<D>;
+  constexpr int TILE = S::TILE, LPT = S::LPT, HPC = S::HPC, CPL = S::CPL, KROW = S::KROW;
 
   const int s = blockIdx.x;
   const int g = blockIdx.y;
@@ -55,212 +90,261 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int nch = (L + p.chunk - 1) / p.chunk;
   if (s >= nch) return;
 
-  __shared__ uint4 k_lds[TILE * LPT];
+  __shared__ uint4 k_lds[TILE * KROW / 4];
   __shared__ uint4 q_lds[GM * LPT];
   __shared__ uint32_t p_lds[(TILE / 2) * GM];
 
+  // heads G .. GM-1 (a group size that is not a power of two) run on zero
+  // queries and are never written
   const uint16_t* qrow = p.q + static_cast<int64_t>(r) * p.q_stride + static_cast<int64_t>(g) * G * D;
-  for (int i = lane; i < G * LPT; i += 64) q_lds[i] = reinterpret_cast<const uint4*>(qrow)[i];
+  for (int i = lane; i < GM * LPT; i += 64)
+    q_lds[i] = (i < G * LPT) ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
 
-  const int32_t* pt = p.page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
+  const int32_t* pt = page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
   const int ps = p.page_size;
-  const int64_t row_elems = static_cast<int64_t>(p.num_kv_heads) * D;
-  const uint16_t* kbase = p.k_cache + static_cast<int64_t>(g) * D;
-  const uint16_t* vbase = p.v_cache + static_cast<int64_t>(g) * D;
+  const int sh = p.page_shift;
+  const uint32_t row_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
+  const uint32_t head_off = static_cast<uint32_t>(g) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(p.k_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(p.v_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
 
   const int t_begin = s * p.chunk;
   const int t_end = min(L, t_begin + p.chunk);
-  const int sub = lane / LPT;  // token subset for p.V
-  const int col = lane % LPT;  // 16-byte column for loads and p.V
+  const int cw = lane % CPL;  // this lane's word of a token row (channels 2cw, 2cw+1)
+  const int qt = lane >> 1;   // q.K layout: token of the tile
+  const int hf = lane & 1;    //              half of the channels
 
-  float m_run[GM], l_run[GM], acc[GM][8];
+  float m_run[GM], l_run[GM], acc[GM][2];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    acc[h][0] = acc[h][1] = 0.f;
   }
   __syncthreads();
 
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(p_lds);
+  uint32_t* k_words = reinterpret_cast<uint32_t*>(k_lds);
+
+  // lane t (mod TILE) returns the byte offset of token t0 + t's row in the
+  // K/V sub-tensor; past the end, the last valid token again (in-bounds
+  // data, weighted by an exact zero below)
+  auto tile_offsets = [&](int t0) -> uint32_t {
+    const int n = min(TILE, t_end - t0);
+    const int tok = t0 + min(lane & (TILE - 1), n - 1);
+    int slot;
+    if (sh >= 0) {
+      slot = (pt[tok >> sh] << sh) + (tok & (ps - 1));
+    } else {
+      const int pg = tok / ps;
+      slot = pt[pg] * ps + (tok - pg * ps);
+    }
+    return static_cast<uint32_t>(min(max(slot, 0), p.num_slots - 1)) * row_bytes;
+  };
+  uint32_t off_cur = tile_offsets(t_begin);
+
   for (int t0 = t_begin; t0 < t_end; t0 += TILE) {
     const int n = min(TILE, t_end - t0);
-    // Lanes past the end reuse the last valid token's slot: in-bounds data,
-    // weighted by an exact zero below.
-    const int tok = t0 + min(lane, n - 1);
-    const int slot = token_slot_safe(pt, tok, ps, p.num_slots);
-    uint4 vr[NI];
+    // page ids of the next tile go out now, so their latency hides behind
+    // this tile
+    const uint32_t off_next = (t0 + TILE < t_end) ? tile_offsets(t0 + TILE) : 0u;
+    // one row load per token, at the token's wave-uniform byte offset
+    uint32_t kw[TILE], vw[TILE];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tl = i * TPI + sub;
-      const int sl = __shfl(slot, tl, 64);
-      const int64_t off = static_cast<int64_t>(sl) * row_elems + col * 8;
-      const uint4 kv = *reinterpret_cast<const uint4*>(kbase + off);
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
-      k_lds[tl * LPT + (col ^ (tl & (LPT - 1)))] = kv;
+    for (int t = 0; t < TILE; ++t)
+      kw[t] = __builtin_amdgcn_raw_buffer_load_b32(krs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), 0);
+#pragma unroll
+    for (int t = 0; t < TILE; ++t)
+      vw[t] = __builtin_amdgcn_raw_buffer_load_b32(vrs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), 0);
+    if (lane < CPL) {
+#pragma unroll
+      for (int t = 0; t < TILE; ++t) k_words[t * KROW + cw] = kw[t];
     }
     __syncthreads();
 
-    // q.K with one token per lane
+    // q.K: lanes 2t and 2t+1 hold token t's two halves.  Each head's q
+    // broadcasts are issued only once the previous head's sum exists (an
+    // empty asm ties the LDS offset to it): the scheduler would otherwise
+    // hoist every head's q reads at once and spill them.
+    uint4 kk[HPC];
+#pragma unroll
+    for (int cc = 0; cc < HPC; ++cc) kk[cc] = k_lds[qt * (KROW / 4) + hf * HPC + cc];
     float sc[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) sc[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < LPT; ++c) {
-      const uint4 kk = k_lds[lane * LPT + (c ^ (lane & (LPT - 1)))];
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const uint4 qq = q_lds[h * LPT + c];
-          float a = sc[h];
-          a = dot2_bf16(kk.x, qq.x, a);
-          a = dot2_bf16(kk.y, qq.y, a);
-          a = dot2_bf16(kk.z, qq.z, a);
-          a = dot2_bf16(kk.w, qq.w, a);
-          sc[h] = a;
-        }
-      }
-    }
-
-    // online softmax, one head at a time; p stored as bf16 pairs of the
-    // two tokens that the p.V lanes combine: (i*TPI+sub, (i+1)*TPI+sub)
-    const bool valid = lane < n;
-    const int ii = lane / TPI, ss = lane % TPI;
-    const int pair = (ii >> 1) * TPI + ss;
-    uint16_t* p16 = reinterpret_cast<uint16_t*>(p_lds);
+    int qoff = hf * HPC;
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        const float x = valid ? sc[h] * p.scale_log2 : -INFINITY;
-        const float mnew = fmaxf(m_run[h], wave_max(x));
-        const float alpha = fast_exp2(m_run[h] - mnew);
-        const uint16_t pb = f32_to_bf16(fast_exp2(x - mnew));
-        l_run[h] = l_run[h] * alpha + bf16_to_f32(pb);
-        m_run[h] = mnew;
+      if (h > 0) asm volatile("" : "+v"(qoff) : "v"(sc[h - 1]));
+      else asm volatile("" : "+v"(qoff));
+      float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
-        p16[(pair * GM + h) * 2 + (ii & 1)] = pb;
+      for (int cc = 0; cc < HPC; ++cc) {
+        const uint4 qq = q_lds[qoff + h * LPT + cc];
+        a = dot2_bf16(kk[cc].x, qq.x, a);
+        a = dot2_bf16(kk[cc].y, qq.y, a);
+        a = dot2_bf16(kk[cc].z, qq.z, a);
+        a = dot2_bf16(kk[cc].w, qq.w, a);
       }
+      sc[h] = a;
+    }
+
+    const bool valid = qt < n;
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float full = sc[h] + dpp_mov<kDppXor1>(sc[h]);
+      const float x = valid ? full * p.scale_log2 : -INFINITY;
+      const float mnew = fmaxf(m_run[h], wave_max(x));
+      const float alpha = fast_exp2(m_run[h] - mnew);
+      const uint16_t pb = f32_to_bf16(fast_exp2(x - mnew));
+      // both lanes of a token hold the same p: count it once, store it
+      // from both (same value)
+      l_run[h] = l_run[h] * alpha + (hf ? 0.f : bf16_to_f32(pb));
+      m_run[h] = mnew;
+      acc[h][0] *= alpha;
+      acc[h][1] *= alpha;
+      p16[((qt >> 1) * GM + h) * 2 + (qt & 1)] = pb;
     }
     __syncthreads();
 
-    // p.V on token pairs
+    // p.V on token pairs (2j, 2j+1)
 #pragma unroll
-    for (int i = 0; i < NI; i += 2) {
-      const uint4 va = vr[i], vb = vr[i + 1];
-      const uint32_t lo[4] = {pair_lo(va.x, vb.x), pair_lo(va.y, vb.y), pair_lo(va.z, vb.z),
-                              pair_lo(va.w, vb.w)};
-      const uint32_t hi[4] = {pair_hi(va.x, vb.x), pair_hi(va.y, vb.y), pair_hi(va.z, vb.z),
-                              pair_hi(va.w, vb.w)};
-      const int pr = (i >> 1) * TPI + sub;
+    for (int j = 0; j < TILE / 2; ++j) {
+      const uint32_t lo = pair_lo(vw[2 * j], vw[2 * j + 1]);
+      const uint32_t hi = pair_hi(vw[2 * j], vw[2 * j + 1]);
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const uint32_t pp = p_lds[pr * GM + h];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            acc[h][2 * k] = dot2_bf16(lo[k], pp, acc[h][2 * k]);
-            acc[h][2 * k + 1] = dot2_bf16(hi[k], pp, acc[h][2 * k + 1]);
-          }
-        }
+        const uint32_t pp = p_lds[j * GM + h];
+        acc[h][0] = dot2_bf16(lo, pp, acc[h][0]);
+        acc[h][1] = dot2_bf16(hi, pp, acc[h][1]);
       }
     }
-    __syncthreads();
+    __syncthreads();  // k_lds / p_lds are rewritten by the next tile
+    off_cur = off_next;
   }
 
-  // combine the token subsets that share a column, and the per-lane sums
   float l_tot[GM];
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    l_tot[h] = (h < G) ? wave_sum(l_run[h]) : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float a = acc[h][j];
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) a += shfl_xor_f(a, off);
-      acc[h][j] = a;
-    }
-  }
+  for (int h = 0; h < GM; ++h) l_tot[h] = wave_sum(l_run[h]);
   if (nch == 1) {
-    if (lane < LPT) {
-      uint16_t* o = p.out + (static_cast<int64_t>(r) * Hq + g * G) * D + col * 8;
+    if (lane < CPL) {
+      uint16_t* o = p.out + (static_cast<int64_t>(r) * Hq + g * G) * D + 2 * cw;
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h < G) {
           const float inv = 1.f / l_tot[h];
-          uint4 w;
-          w.x = pack_bf16(acc[h][0] * inv, acc[h][1] * inv);
-          w.y = pack_bf16(acc[h][2] * inv, acc[h][3] * inv);
-          w.z = pack_bf16(acc[h][4] * inv, acc[h][5] * inv);
-          w.w = pack_bf16(acc[h][6] * inv, acc[h][7] * inv);
-          *reinterpret_cast<uint4*>(o + h * D) = w;
+          *reinterpret_cast<uint32_t*>(o + h * D) = pack_bf16(acc[h][0] * inv, acc[h][1] * inv);
         }
       }
     }
-  } else {
-    const int64_t base = (static_cast<int64_t>(r) * p.max_chunks + s) * Hq + g * G;
-    if (lane < LPT) {
+    return;
+  }
+  const int64_t base = (static_cast<int64_t>(r) * p.max_chunks + s) * Hq + g * G;
+  if (lane < CPL) {
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          float4* o = reinterpret_cast<float4*>(p.ws_o + (base + h) * D + col * 8);
-          o[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-          o[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-        }
-      }
+    for (int h = 0; h < GM; ++h) {
+      if (h < G)
+        *reinterpret_cast<float2*>(p.ws_o + (base + h) * D + 2 * cw) = make_float2(acc[h][0], acc[h][1]);
     }
-    if (lane == 0) {
+  }
+  if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          p.ws_ml[(base + h) * 2 + 0] = m_run[h];
-          p.ws_ml[(base + h) * 2 + 1] = l_tot[h];
-        }
+    for (int h = 0; h < GM; ++h) {
+      if (h < G) {
+        p.ws_ml[(base + h) * 2 + 0] = m_run[h];
+        p.ws_ml[(base + h) * 2 + 1] = l_tot[h];
       }
     }
   }
 }
 
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the chunks s of
-// one (request, q head); requests with a single chunk were finished above.
+// one (request, q head).  A workgroup of 256 threads per (request, q head):
+// the chunk maxima and weights are reduced across threads, the weights kept
+// in LDS, then 256/(D/4) chunk groups accumulate float4 channel pieces in
+// parallel and are summed through LDS -- a long request's many chunks cost
+// a few memory round trips, not one per chunk.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxChunks = 4096;
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
-  constexpr int CPL = D / 64;  // channels per lane
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+  constexpr int QPH = D / 4;                   // float4 pieces per head
+  constexpr int NG = kMergeThreads / QPH;      // chunk groups
+  const int h = blockIdx.x;                    // q head
   const int r = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int Hq = p.num_kv_heads * p.group;
+  const int tid = threadIdx.x;
   const int L = min(p.seq_lens[r], p.max_seq_len);
   if (L <= 0) return;
-  const int nch = (L + p.chunk - 1) / p.chunk;
+  const int nch = min((L + p.chunk - 1) / p.chunk, kMergeMaxChunks);
   if (nch <= 1) return;
-  const int64_t base = static_cast<int64_t>(r) * p.max_chunks * Hq + h;
+  const int Hq = p.num_kv_heads * p.group;
+  const int64_t base = static_cast<int64_t>(r) * p.max_chunks * Hq + h;  // chunk s at base + s*Hq
+
+  __shared__ float wgt[kMergeMaxChunks];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float4 part[NG][QPH];
+
   float mx = -INFINITY;
-  for (int s = 0; s < nch; ++s) mx = fmaxf(mx, p.ws_ml[(base + static_cast<int64_t>(s) * Hq) * 2]);
-  float den = 0.f, num[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) num[c] = 0.f;
-  for (int s = 0; s < nch; ++s) {
-    const int64_t idx = base + static_cast<int64_t>(s) * Hq;
-    const float w = fast_exp2(p.ws_ml[idx * 2] - mx);
-    den += w * p.ws_ml[idx * 2 + 1];
-    const float* o = p.ws_o + idx * D + lane * CPL;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) num[c] += w * o[c];
+  for (int s = tid; s < nch; s += kMergeThreads) mx = fmaxf(mx, p.ws_ml[(base + static_cast<int64_t>(s) * Hq) * 2]);
+  mx = block_reduce(mx, red, true);
+  float den = 0.f;
+  for (int s = tid; s < nch; s += kMergeThreads) {
+    const int64_t u = base + static_cast<int64_t>(s) * Hq;
+    const float w = fast_exp2(p.ws_ml[u * 2] - mx);
+    wgt[s] = w;
+    den += w * p.ws_ml[u * 2 + 1];
   }
-  const float inv = 1.f / den;
-  uint16_t* out = p.out + (static_cast<int64_t>(r) * Hq + h) * D + lane * CPL;
+  den = block_reduce(den, red, false);  // its barriers also publish wgt[]
+
+  const int cq = tid % QPH;  // float4 piece of the head
+  const int cg = tid / QPH;  // chunk group
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = cg; s < nch; s += NG) {
+    const float w = wgt[s];
+    const float4 o = reinterpret_cast<const float4*>(p.ws_o + (base + static_cast<int64_t>(s) * Hq) * D)[cq];
+    acc.x += w * o.x;
+    acc.y += w * o.y;
+    acc.z += w * o.z;
+    acc.w += w * o.w;
+  }
+  part[cg][cq] = acc;
+  __syncthreads();
+  if (tid < QPH) {
+    float4 t = part[0][tid];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) out[c] = f32_to_bf16(num[c] * inv);
+    for (int i = 1; i < NG; ++i) {
+      t.x += part[i][tid].x;
+      t.y += part[i][tid].y;
+      t.z += part[i][tid].z;
+      t.w += part[i][tid].w;
+    }
+    const float inv = 1.f / den;
+    uint2 wv;
+    wv.x = pack_bf16(t.x * inv, t.y * inv);
+    wv.y = pack_bf16(t.z * inv, t.w * inv);
+    *reinterpret_cast<uint2*>(p.out + (static_cast<int64_t>(r) * Hq + h) * D + 4 * tid) = wv;
+  }
 }
 
 template <int D, int GM>
 static void launch_decode_t(const DecodeParams& p, int batch, hipStream_t stream) {
   const dim3 grid(p.max_chunks, p.num_kv_heads, batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, GM>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, GM>), grid, dim3(64), 0, stream, p, p.page_table);
   if (p.max_chunks > 1) {
     const dim3 mgrid(p.num_kv_heads * p.group, batch);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(kMergeThreads), 0, stream, p);
   }
 }
 
