@@ -41,6 +41,10 @@
  *     elements) for the attention calls; store_kv accepts any alignment.
  *   - Padding conventions for fixed-size batches: out_loc[t] < 0 skips row
  *     t; seq_lens[r] == 0 in decode writes zeros and reads no KV.
+ *   - The attention calls address one (K or V, layer) sub-tensor of the pool
+ *     with 32-bit byte offsets: num_pages*page_size*num_kv_heads*head_dim*2
+ *     must be below 2^32 (MSGL_ERR_UNSUPPORTED otherwise); larger pools can
+ *     be split into several pool structs.  sm_scale must be > 0.
  */
 #ifndef MSGL_H
 #define MSGL_H

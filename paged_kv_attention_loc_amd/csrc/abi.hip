@@ -50,6 +50,13 @@ msgl_status check_pool(const msgl_kv_pool* pool, int32_t layer) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// log2(page_size) when it is a power of two, else -1 (the kernels then divide)
+int32_t page_shift_of(int32_t page_size) {
+  for (int b = 0; b < 31; ++b)
+    if (page_size == (1 << b)) return b;
+  return -1;
+}
+
 int64_t num_slots(const msgl_kv_pool* pool) {
   return static_cast<int64_t>(pool->num_pages) * pool->page_size;
 }
@@ -222,6 +229,7 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   st = check_attention_geometry(pool, num_qo_heads);
   if (st != MSGL_OK) return st;
   if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f)) return MSGL_ERR_SHAPE;
   // decode addresses one (K or V, layer) sub-tensor with 32-bit byte offsets
   if (half_elems(pool) * 2 >= (int64_t{1} << 32)) return MSGL_ERR_UNSUPPORTED;
   const int32_t d = pool->head_dim;
@@ -265,9 +273,7 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   if (p.max_chunks < 1) p.max_chunks = 1;
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
-  p.page_shift = -1;
-  for (int b = 0; b < 31; ++b)
-    if (pool->page_size == (1 << b)) p.page_shift = b;
+  p.page_shift = page_shift_of(pool->page_size);
   p.max_seq_len = max_seq_len;
   p.scale_log2 = sm_scale * kLog2e;
   if (need > 0) {
@@ -305,6 +311,9 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
       !aligned16(q) || !aligned16(out))
     return MSGL_ERR_SHAPE;
   if (max_extend_len > max_seq_len) return MSGL_ERR_SHAPE;
+  // extend addresses one (K or V, layer) sub-tensor with 32-bit byte offsets
+  if (half_elems(pool) * 2 >= (int64_t{1} << 32)) return MSGL_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f)) return MSGL_ERR_SHAPE;
   if (page_table_stride < 1) return MSGL_ERR_SHAPE;
   const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
   if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
@@ -343,6 +352,8 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
   p.group = G;
   p.page_size = pool->page_size;
   p.num_mtiles = static_cast<int32_t>(mtiles);
+  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
+  p.page_shift = page_shift_of(pool->page_size);
   p.max_extend_len = max_extend_len;
   p.max_seq_len = max_seq_len;
   p.num_slots = static_cast<int32_t>(num_slots(pool));

@@ -19,16 +19,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // a.lo*b.lo + a.hi*b.hi + c, bf16 pairs in 32-bit words, fp32 accumulate.
@@ -178,9 +176,11 @@ struct ExtendParams {
   int32_t group;
   int32_t page_size;
   int32_t num_mtiles;
+  int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
   int32_t max_extend_len;
   int32_t max_seq_len;
   int32_t num_slots;
+  uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
   float scale_log2;
 };
 

@@ -117,6 +117,10 @@ def test_decode_rejects_bad_arguments_without_launch():
     assert _decode(lib, p, batch=-1) == SHAPE
     assert _decode(lib, p, batch=0) == OK
     assert _decode(lib, p, layer=5) == SHAPE
+    assert _decode(lib, p, scale=0.0) == SHAPE
+    assert _decode(lib, p, scale=float("nan")) == SHAPE
+    # one (K or V, layer) sub-tensor of 2^32 bytes or more
+    assert _decode(lib, _pool(num_kv_heads=8, num_pages=1 << 17, page_size=16)) == UNSUP
 
 
 def _extend(lib, pool, **kw):
@@ -140,6 +144,8 @@ def test_extend_rejects_bad_arguments_without_launch():
     assert _extend(lib, p, max_ext=5000) == SHAPE  # extend longer than the sequence bound
     assert _extend(lib, p, pt_stride=10) == SHAPE
     assert _extend(lib, p, out=FAKE + 2) == SHAPE
+    assert _extend(lib, p, scale=-0.1) == SHAPE
+    assert _extend(lib, _pool(num_kv_heads=8, num_pages=1 << 17, page_size=16)) == UNSUP
     assert _extend(lib, p, total=0) == OK
     assert _extend(lib, p, batch=0) == OK
 
