@@ -90,6 +90,13 @@ msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_he
 // kMaxDecodeSplits splits -- the merge kernel keeps one weight per split in
 // LDS.
 constexpr int64_t kMaxDecodeSplits = 4096;
+// Waves per extend workgroup (32 query rows each): 8 by default;
+// MSGL_EXTEND_WAVES=4 selects 128-row workgroups.
+int extend_waves() {
+  const char* v = std::getenv("MSGL_EXTEND_WAVES");
+  return (v && std::atoi(v) == 4) ? 4 : 8;
+}
+
 int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_seq_len) {
   int64_t c = 64;
   const char* v = std::getenv("MSGL_DECODE_SPLIT");
@@ -318,8 +325,10 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
   const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
   if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
   const int32_t G = num_qo_heads / pool->num_kv_heads;
-  const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + 127) / 128;
-  if (mtiles > INT32_MAX) return MSGL_ERR_UNSUPPORTED;
+  const int waves = extend_waves();
+  const int64_t rows_per_tile = 32 * waves;
+  const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + rows_per_tile - 1) / rows_per_tile;
+  if (mtiles > 65535) return MSGL_ERR_UNSUPPORTED;  // grid z
   st = check_device();
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
@@ -358,7 +367,7 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
   p.max_seq_len = max_seq_len;
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.scale_log2 = sm_scale * kLog2e;
-  return hip_status(launch_extend(p, d, batch, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_extend(p, d, batch, waves, static_cast<hipStream_t>(stream)));
 }
 
 msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,

@@ -89,6 +89,17 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
 
+// max / sum of x over lanes l and l^32 (one v_permlane32_swap: lanes 0-31
+// receive the upper half's values and vice versa).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // --------------------------------------------------- page-table translation
 // Slot of logical token `tok` of the request whose page_table row is `row`:
 // page_table[row][tok / page_size] * page_size + tok % page_size.
@@ -188,6 +199,9 @@ struct ExtendParams {
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStream_t stream);
-hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, hipStream_t stream);
+// `waves` (4 or 8) sets the query rows per workgroup (32 per wave); the
+// caller sizes p.num_mtiles for it.
+hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,
+                         hipStream_t stream);
 
 }  // namespace msgl
