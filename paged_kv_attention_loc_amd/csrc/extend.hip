@@ -246,17 +246,39 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
     if (wave_rows && n0 <= wlim_hi) {
       const uint8_t* kt = k_rd + (t & 1) * BUF;
       const uint8_t* vt = v_rd + (t & 1) * BUF;
-      // ---- S^T = K Q^T: two 32-key blocks
+      // ---- S^T = K Q^T: two 32-key blocks.  The K operands of block 1 are
+      // read while block 0 multiplies, and the V^T operands of the first
+      // channel block while block 1 does (the scheduling groups pin that
+      // order: LDS reads stay several MFMAs ahead of their use)
       f32x16_t sc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+      bf16x8_t ka[KS];
+      bf16x8_t va[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kb * 32 * K_ROW + ks * 32);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], sc[kb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + ks * 32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[0], 0, 0, 0);
+        ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + 32 * K_ROW + ks * 32);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[1], 0, 0, 0);
+        if (ks < 4) va[ks] = *reinterpret_cast<const bf16x8_t*>(vt + ks * 32);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       // ---- causal mask on tiles that cross a row's limit
       if (n0 + BN - 1 > wlim_lo) {
@@ -304,15 +326,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
           for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
       }
       l_run += lsum;
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T; the next channel block's operands are read one
+      // MFMA ahead
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + cb * 32 * V_ROW + kk * 32);
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kk], o[cb], 0, 0, 0);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], pop[kk], o[cb], 0, 0, 0);
+          if (cb + 1 < CB)
+            va[kk] = *reinterpret_cast<const bf16x8_t*>(vt + (cb + 1) * 32 * V_ROW + kk * 32);
         }
       }
+#pragma unroll
+      for (int i = 0; i < 4 * (CB - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     // tile t+1: registers -> the other stage; then tile t+2's loads, tile
     // t+3's offsets and tile t+4's page entries go out
