@@ -121,17 +121,20 @@ def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
     q_d = bits(ph_dec.q)
     with threadpool_limits(limits=cores):
         blas = [i.get("num_threads") for i in threadpool_info()]
-        # decode: requests in order, until half the budget is spent
+        # decode: requests in order, passing over the batch again until half
+        # the budget is spent
         t0 = time.perf_counter()
         done = []
-        for r in range(ph_dec.batch):
-            sel = np.array([r])
-            oracle.paged_decode(pool_d, 0, q_d[sel], wl_dec.page_table, ph_dec.table_idx[sel],
-                                ph_dec.seq_lens[sel])
-            done.append(r)
-            if time.perf_counter() - t0 > budget_s / 2:
-                break
+        while time.perf_counter() - t0 <= budget_s / 2:
+            for r in range(ph_dec.batch):
+                sel = np.array([r])
+                oracle.paged_decode(pool_d, 0, q_d[sel], wl_dec.page_table, ph_dec.table_idx[sel],
+                                    ph_dec.seq_lens[sel])
+                done.append(r)
+                if time.perf_counter() - t0 > budget_s / 2:
+                    break
         t_dec = time.perf_counter() - t0
+        passes = len(done) / ph_dec.batch
         L = ph_dec.seq_lens[done].astype(np.int64)
         dec_b = int((L * 2 * wl_dec.num_kv_heads * wl_dec.head_dim * 2).sum()
                     + 2 * len(done) * wl_dec.num_qo_heads * wl_dec.head_dim * 2
@@ -157,8 +160,8 @@ def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
         "cores": cores,
         "blas_threads": blas,
         "kind": "oracle",
-        "sample": (f"decode: {len(done)} of {ph_dec.batch} requests of the Llama-3-8B decode "
-                   f"batch ({int(L.sum())} KV tokens, {t_dec:.1f} s); extend: {len(rows)} of "
+        "sample": (f"decode: {passes:.2f} passes over the {ph_dec.batch} requests of the Llama-3-8B "
+                   f"decode batch ({int(L.sum())} KV tokens, {t_dec:.1f} s); extend: {len(rows)} of "
                    f"{ph_ext.num_tokens} query rows of the radix-shared extend ({t_ext:.1f} s)"),
         "extend_value": round(ext_f / t_ext / 1e9, 4),
         "extend_unit": "GFLOP/s",
