@@ -97,8 +97,11 @@ int extend_waves() {
   return (v && std::atoi(v) == 4) ? 4 : 8;
 }
 
+// Tokens per decode split (a multiple of 64): 256 by default, measured best
+// on the Llama-3-8B and Qwen3-30B-A3B geometry batches; MSGL_DECODE_SPLIT
+// overrides it.
 int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_seq_len) {
-  int64_t c = 64;
+  int64_t c = 256;
   const char* v = std::getenv("MSGL_DECODE_SPLIT");
   if (v && v[0]) {
     const long e = std::strtol(v, nullptr, 10);
@@ -216,7 +219,8 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
   const int32_t chunk = decode_chunk(batch, num_kv_heads, max_seq_len);
   const int64_t mc = (static_cast<int64_t>(max_seq_len) + chunk - 1) / chunk;
   if (mc <= 1) return 0;
-  const int64_t units = static_cast<int64_t>(batch) * mc * num_qo_heads;
+  // one unit of padding per (request, chunk) row: see decode_split_kernel
+  const int64_t units = static_cast<int64_t>(batch) * mc * (num_qo_heads + 1);
   const int64_t o_bytes = units * head_dim * 4;
   const int64_t ml_bytes = units * 2 * 4;
   return static_cast<size_t>(((o_bytes + 255) / 256) * 256 + ml_bytes);
@@ -284,7 +288,7 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   p.max_seq_len = max_seq_len;
   p.scale_log2 = sm_scale * kLog2e;
   if (need > 0) {
-    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * num_qo_heads;
+    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * (num_qo_heads + 1);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     p.ws_o = reinterpret_cast<float*>(ws);
     p.ws_ml = reinterpret_cast<float*>(ws + ((units * d * 4 + 255) / 256) * 256);

@@ -11,9 +11,9 @@
 // One wave64 workgroup handles (request, kv head, chunk of `chunk` tokens)
 // in tiles of 32 tokens.  A wave needs about 9-11 KiB of LDS and few
 // registers, so a CU holds 16 of them and their loads overlap each other's
-// arithmetic; chunks are short (64 tokens by default) so that many
-// independent waves are in flight -- measured faster than fewer, longer
-// waves despite the extra partials.
+// arithmetic; chunks are short (256 tokens by default) so that many
+// independent waves are in flight while the split partials stay a few
+// percent of the KV bytes.
 //   * addressing: one vector load per tile fetches the tile's page ids
 //     (lane t: token t), one tile ahead; each token's row byte offset is
 //     then moved into an SGPR (v_readlane) and every K/V load is a buffer
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
     }
     return;
   }
-  const int64_t base = (static_cast<int64_t>(r) * p.max_chunks + s) * Hq + g * G;
+  const int64_t base = (static_cast<int64_t>(r) * p.max_chunks + s) * (Hq + 1) + g * G;
   if (lane < CPL) {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
@@ -289,18 +289,21 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int nch = min((L + p.chunk - 1) / p.chunk, kMergeMaxChunks);
   if (nch <= 1) return;
   const int Hq = p.num_kv_heads * p.group;
-  const int64_t base = static_cast<int64_t>(r) * p.max_chunks * Hq + h;  // chunk s at base + s*Hq
+  // chunk s at base + s*(Hq+1): one unit of padding per chunk keeps the
+  // chunk stride off powers of two
+  const int64_t base = static_cast<int64_t>(r) * p.max_chunks * (Hq + 1) + h;
 
   __shared__ float wgt[kMergeMaxChunks];
   __shared__ float red[kMergeThreads / 64];
   __shared__ float4 part[NG][QPH];
 
   float mx = -INFINITY;
-  for (int s = tid; s < nch; s += kMergeThreads) mx = fmaxf(mx, p.ws_ml[(base + static_cast<int64_t>(s) * Hq) * 2]);
+  for (int s = tid; s < nch; s += kMergeThreads)
+    mx = fmaxf(mx, p.ws_ml[(base + static_cast<int64_t>(s) * (Hq + 1)) * 2]);
   mx = block_reduce(mx, red, true);
   float den = 0.f;
   for (int s = tid; s < nch; s += kMergeThreads) {
-    const int64_t u = base + static_cast<int64_t>(s) * Hq;
+    const int64_t u = base + static_cast<int64_t>(s) * (Hq + 1);
     const float w = fast_exp2(p.ws_ml[u * 2] - mx);
     wgt[s] = w;
     den += w * p.ws_ml[u * 2 + 1];
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 #pragma unroll 4
   for (int s = cg; s < nch; s += NG) {
     const float w = wgt[s];
-    const float4 o = reinterpret_cast<const float4*>(p.ws_o + (base + static_cast<int64_t>(s) * Hq) * D)[cq];
+    const float4 o = reinterpret_cast<const float4*>(p.ws_o + (base + static_cast<int64_t>(s) * (Hq + 1)) * D)[cq];
     acc.x += w * o.x;
     acc.y += w * o.y;
     acc.z += w * o.z;
@@ -340,7 +343,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 
 template <int D, int GM>
 static void launch_decode_t(const DecodeParams& p, int batch, hipStream_t stream) {
-  const dim3 grid(p.max_chunks, p.num_kv_heads, batch);
+  // an odd grid width: with a multiple of 8 chunk columns every chunk
+  // index lands on the same XCD in every row (workgroups are dealt to the 8
+  // XCDs round-robin), which measured up to 1.6x slower
+  const dim3 grid(p.max_chunks | 1, p.num_kv_heads, batch);
   hipLaunchKernelGGL((decode_split_kernel<D, GM>), grid, dim3(64), 0, stream, p, p.page_table);
   if (p.max_chunks > 1) {
     const dim3 mgrid(p.num_kv_heads * p.group, batch);
