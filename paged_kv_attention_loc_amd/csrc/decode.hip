@@ -257,87 +257,64 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
 }
 
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the chunks s of
-// one (request, q head).  A workgroup of 256 threads per (request, q head):
-// the chunk maxima and weights are reduced across threads, the weights kept
-// in LDS, then 256/(D/4) chunk groups accumulate float4 channel pieces in
-// parallel and are summed through LDS -- a long request's many chunks cost
-// a few memory round trips, not one per chunk.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeMaxChunks = 4096;
-
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  v = is_max ? wave_max(v) : wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-  return r;
-}
+// one (request, q head), with M the largest chunk maximum.  One wave per
+// (request, q head): lane l owns float4 piece l % (D/4) of the head and the
+// chunks s = l / (D/4) (mod 64 / (D/4)); the lanes that share a piece are
+// joined by exchanges 32 (and 16) lanes apart.
+constexpr int kMergeThreads = 64;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  constexpr int QPH = D / 4;                   // float4 pieces per head
-  constexpr int NG = kMergeThreads / QPH;      // chunk groups
-  const int h = blockIdx.x;                    // q head
+  constexpr int QPH = D / 4;          // float4 pieces per head
+  constexpr int NH = 64 / QPH;        // lanes per piece (chunk phases)
+  const int h = blockIdx.x;           // q head
   const int r = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int L = min(p.seq_lens[r], p.max_seq_len);
   if (L <= 0) return;
-  const int nch = min((L + p.chunk - 1) / p.chunk, kMergeMaxChunks);
+  const int nch = (L + p.chunk - 1) / p.chunk;
   if (nch <= 1) return;
   const int Hq = p.num_kv_heads * p.group;
   // chunk s at base + s*(Hq+1): one unit of padding per chunk keeps the
   // chunk stride off powers of two
   const int64_t base = static_cast<int64_t>(r) * p.max_chunks * (Hq + 1) + h;
-
-  __shared__ float wgt[kMergeMaxChunks];
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float4 part[NG][QPH];
+  const int64_t row = Hq + 1;
+  const int cq = lane % QPH;
+  const int ph = lane / QPH;
 
   float mx = -INFINITY;
-  for (int s = tid; s < nch; s += kMergeThreads)
-    mx = fmaxf(mx, p.ws_ml[(base + static_cast<int64_t>(s) * (Hq + 1)) * 2]);
-  mx = block_reduce(mx, red, true);
-  float den = 0.f;
-  for (int s = tid; s < nch; s += kMergeThreads) {
-    const int64_t u = base + static_cast<int64_t>(s) * (Hq + 1);
-    const float w = fast_exp2(p.ws_ml[u * 2] - mx);
-    wgt[s] = w;
-    den += w * p.ws_ml[u * 2 + 1];
-  }
-  den = block_reduce(den, red, false);  // its barriers also publish wgt[]
+  for (int s = lane; s < nch; s += 64) mx = fmaxf(mx, p.ws_ml[(base + s * row) * 2]);
+  mx = wave_max(mx);
 
-  const int cq = tid % QPH;  // float4 piece of the head
-  const int cg = tid / QPH;  // chunk group
+  float den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-  for (int s = cg; s < nch; s += NG) {
-    const float w = wgt[s];
-    const float4 o = reinterpret_cast<const float4*>(p.ws_o + (base + static_cast<int64_t>(s) * (Hq + 1)) * D)[cq];
+  for (int s = ph; s < nch; s += NH) {
+    const int64_t u = base + s * row;
+    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + u * 2);
+    const float w = fast_exp2(ml.x - mx);
+    den += w * ml.y;
+    const float4 o = reinterpret_cast<const float4*>(p.ws_o + u * D)[cq];
     acc.x += w * o.x;
     acc.y += w * o.y;
     acc.z += w * o.z;
     acc.w += w * o.w;
   }
-  part[cg][cq] = acc;
-  __syncthreads();
-  if (tid < QPH) {
-    float4 t = part[0][tid];
+  // join the NH lanes of each piece (their den values differ per phase)
 #pragma unroll
-    for (int i = 1; i < NG; ++i) {
-      t.x += part[i][tid].x;
-      t.y += part[i][tid].y;
-      t.z += part[i][tid].z;
-      t.w += part[i][tid].w;
-    }
+  for (int off = 32; off >= QPH; off >>= 1) {
+    den += shfl_xor_f(den, off);
+    acc.x += shfl_xor_f(acc.x, off);
+    acc.y += shfl_xor_f(acc.y, off);
+    acc.z += shfl_xor_f(acc.z, off);
+    acc.w += shfl_xor_f(acc.w, off);
+  }
+  if (lane < QPH) {
     const float inv = 1.f / den;
     uint2 wv;
-    wv.x = pack_bf16(t.x * inv, t.y * inv);
-    wv.y = pack_bf16(t.z * inv, t.w * inv);
-    *reinterpret_cast<uint2*>(p.out + (static_cast<int64_t>(r) * Hq + h) * D + 4 * tid) = wv;
+    wv.x = pack_bf16(acc.x * inv, acc.y * inv);
+    wv.y = pack_bf16(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(p.out + (static_cast<int64_t>(r) * Hq + h) * D + 4 * lane) = wv;
   }
 }
 
