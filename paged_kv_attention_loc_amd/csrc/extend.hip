@@ -20,25 +20,24 @@
 //     in its own L2; the heaviest row tiles are launched first;
 //   * K/V tiles are double-buffered in LDS, one barrier per tile.  While
 //     tile t is computed, tile t+1 is in registers on its way to the other
-//     buffer, the row offsets of tile t+2 wait in LDS, and the page-table
-//     entries of tile t+3 are in flight;
-//   * a tile's row offsets (slot * row bytes) are computed once, by one
-//     thread per key, and shared through LDS; rows are read with buffer
-//     loads at 32-bit offsets inside the (K or V, layer) sub-tensor, whose
-//     range check also absorbs a wild page id;
+//     buffer and the page-table entries of tile t+2 are in flight;
+//   * every loading thread owns 4 consecutive keys and one 16-byte column,
+//     for K and for V alike; rows are read with buffer loads at 32-bit
+//     offsets inside the (K or V, layer) sub-tensor, whose range check
+//     also absorbs a wild page id;
 //   * each wave computes S^T = K Q^T, so a lane holds one query column and
 //     16 keys per 32-key block: the row maximum and sum need one exchange
 //     with the lane 32 apart (v_permlane32_swap);
-//   * K is staged row-major, V transposed (channel-major) so that the A
-//     operand of O^T = V^T P^T is one 16-byte LDS read; inside every
-//     16-key group V^T keeps the keys in the order in which the S^T
-//     accumulator registers hold them, so P^T feeds the second MFMA
-//     straight from registers.  Both layouts pad their rows by 16 bytes:
-//     with 64 four-byte banks that makes the 16-lane groups of every read
-//     and write hit distinct banks, and every LDS address is a per-lane
-//     base plus a compile-time offset.  K and V use different loader
-//     mappings (16 lanes per K row; 16 key groups per V^T row) for the
-//     same reason;
+//   * K and V are both staged row-major.  The A operand of O^T = V^T P^T
+//     is read with two ds_read_b64_tr_b16 (the LDS transpose read of
+//     CDNA4: in each 16-lane group, lane i receives element i%4 of the
+//     8-byte pieces addressed by lanes 4j + i/4, j = 0..3), which turns
+//     four key rows into four keys of one channel per lane, in the order
+//     in which the S^T accumulator registers hold the keys -- so P^T feeds
+//     the second MFMA straight from registers.  K rows are padded by 16
+//     bytes and V rows by 64: with 64 four-byte banks every 16-lane read
+//     and write hits distinct banks, and every LDS address is a per-lane
+//     base plus a compile-time offset;
 //   * the running maximum only moves when a row's new maximum exceeds it by
 //     more than 2^8 in exp2 terms, so the O rescale is rare; masking runs
 //     only on tiles that cross a row's causal limit.
@@ -48,12 +47,13 @@ namespace msgl {
 
 namespace {
 
-// Physical start position (within a 16-key group) of the 4-key group kq:
-// S^T registers hold keys {0-3, 8-11} in lanes 0-31 and {4-7, 12-15} in
-// lanes 32-63, so groups 0,1,2,3 go to positions 0,8,4,12.
-__device__ __forceinline__ int vt_group_pos(int kq) {
-  const int j = kq & 3;
-  return 16 * (kq >> 2) + 4 * (((j & 1) << 1) | (j >> 1));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// ds_read_b64_tr_b16 at byte address `addr` of the LDS window
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(__attribute__((address_space(3))) const uint8_t*)(addr));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t extend_rsrc(const void* base, uint32_t bytes) {
@@ -75,9 +75,9 @@ struct ExtendShape {
   static constexpr int KS = D / 16;       // MFMA k-steps of Q.K^T
   static constexpr int CB = D / 32;       // 32-channel blocks of the output
   static constexpr int K_ROW = D * 2 + 16;   // bytes per staged K row
-  static constexpr int V_ROW = BN * 2 + 16;  // bytes per staged V^T row
+  static constexpr int V_ROW = D * 2 + 64;   // bytes per staged V row
   static constexpr int K_BYTES = BN * K_ROW;
-  static constexpr int V_BYTES = D * V_ROW;
+  static constexpr int V_BYTES = BN * V_ROW;
   static constexpr int BUF = K_BYTES + V_BYTES;   // one pipeline stage
   static constexpr int LOADERS = (BN / 4) * NCOL;  // threads that load a tile
   static_assert(LOADERS <= 64 * WAVES, "not enough threads to load a tile");
@@ -112,7 +112,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const int Hq = p.num_kv_heads * G;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint32_t row_off[2][BN];
 
   // this lane's query row (rows past the end are clamped and not written)
   const int mrow = m0 + w * 32 + q32;
@@ -145,67 +144,50 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const __amdgpu_buffer_rsrc_t vrs =
       extend_rsrc(p.v_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
 
-  // row offsets: thread `tid` < BN owns key t*BN + tid (clamped to the last
-  // key, whose row is valid; keys past kv_end are masked for every row)
-  int ent = 0;
-  auto off_key = [&](int t) { return min(t * BN + tid, kv_end - 1); };
-  auto fetch_entry = [&](int t) {
-    if (tid < BN) {
-      const int key = off_key(t);
-      ent = POW2 ? pt[key >> sh] : pt[key / ps];
-    }
-  };
-  auto publish_offsets = [&](int t) {
-    if (tid < BN) {
-      const int key = off_key(t);
-      const int slot = POW2 ? (ent << sh) + (key & (ps - 1)) : ent * ps + key % ps;
-      row_off[t & 1][tid] = static_cast<uint32_t>(slot) * row_bytes;
-    }
-  };
-
-  // loader roles: K -- keys 4kqk .. 4kqk+3, 16-byte column cgk (16 lanes
-  // cover one row); V -- keys 4kqv .. 4kqv+3, column cgv (16 lanes cover
-  // the 16 key groups of one channel column)
+  // loader role: keys 4kq .. 4kq+3 of a tile, 16-byte column cg, for K and
+  // V alike.  Its page entries are fetched a tile ahead of the row loads;
+  // keys past kv_end are clamped to the last key, whose row is valid
+  // (those keys are masked for every row).
   const bool loader = tid < S::LOADERS;
-  const int kqk = tid / NCOL, cgk = tid % NCOL;
-  const int kqv = tid & 15, cgv = tid >> 4;
+  const int kq = tid / NCOL;
+  const int cg = tid % NCOL;
+  // with a power-of-two page size of at least 4 the four keys share a page
+  const bool one_page = POW2 && ps >= 4;
+  int ent[4];
+  auto tile_key = [&](int t, int j) { return min(t * BN + 4 * kq + j, kv_end - 1); };
+  auto fetch_entries = [&](int t) {
+    if (one_page) {
+      ent[0] = pt[tile_key(t, 0) >> sh];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = tile_key(t, j);
+        ent[j] = POW2 ? pt[key >> sh] : pt[key / ps];
+      }
+    }
+  };
   uint4 kr[4], vr[4];
-  auto issue_loads = [&](int t) {
-    const uint4 ko = *reinterpret_cast<const uint4*>(&row_off[t & 1][4 * kqk]);
-    const uint4 vo = *reinterpret_cast<const uint4*>(&row_off[t & 1][4 * kqv]);
-    const uint32_t kof[4] = {ko.x, ko.y, ko.z, ko.w};
-    const uint32_t vof[4] = {vo.x, vo.y, vo.z, vo.w};
+  auto issue_loads = [&](int t) {  // tile t's rows, using the entries in ent
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(krs, kof[j] + cgk * 16, 0, 0);
-      const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(vrs, vof[j] + cgv * 16, 0, 0);
+      const int key = tile_key(t, j);
+      const int e = one_page ? ent[0] : ent[j];
+      const int slot = POW2 ? (e << sh) + (key & (ps - 1)) : e * ps + key % ps;
+      const uint32_t off = static_cast<uint32_t>(slot) * row_bytes + cg * 16;
+      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
       kr[j] = make_uint4(a.x, a.y, a.z, a.w);
       vr[j] = make_uint4(b.x, b.y, b.z, b.w);
     }
   };
-  // registers -> LDS stage b: K rows, then V transposed with 4 keys per
-  // 8-byte write
-  uint8_t* const k_st = lds + kqk * 4 * K_ROW + cgk * 16;
-  uint8_t* const v_st = lds + K_BYTES + cgv * 8 * V_ROW + vt_group_pos(kqv) * 2;
+  // registers -> LDS stage b: K and V rows
+  uint8_t* const k_st = lds + kq * 4 * K_ROW + cg * 16;
+  uint8_t* const v_st = lds + K_BYTES + kq * 4 * V_ROW + cg * 16;
   auto store_tile = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(k_st + b * BUF + j * K_ROW) = kr[j];
-    const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-    const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-    const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-    const uint32_t* a3 = reinterpret_cast<const uint32_t*>(&vr[3]);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int wi = c >> 1;
-      uint2 wv;
-      if (c & 1) {
-        wv.x = pair_hi(a0[wi], a1[wi]);
-        wv.y = pair_hi(a2[wi], a3[wi]);
-      } else {
-        wv.x = pair_lo(a0[wi], a1[wi]);
-        wv.y = pair_lo(a2[wi], a3[wi]);
-      }
-      *reinterpret_cast<uint2*>(v_st + b * BUF + c * V_ROW) = wv;
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint4*>(k_st + b * BUF + j * K_ROW) = kr[j];
+      *reinterpret_cast<uint4*>(v_st + b * BUF + j * V_ROW) = vr[j];
     }
   };
 
@@ -217,20 +199,19 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // prologue: offsets of tiles 0 and 1 in LDS, tile 0 staged, tile 1 in
-  // registers, tile 2's offsets published and tile 3's entries in flight
-  fetch_entry(0);
-  publish_offsets(0);
-  if (ntiles > 1) fetch_entry(1);
+  // prologue: tile 0 staged, tile 1 in registers, tile 2's entries in
+  // flight
+  if (loader) {
+    fetch_entries(0);
+    issue_loads(0);
+    if (ntiles > 1) fetch_entries(1);
+    store_tile(0);
+  }
   __syncthreads();
-  if (loader) issue_loads(0);
-  if (ntiles > 1) publish_offsets(1);
-  if (ntiles > 2) fetch_entry(2);
-  if (loader) store_tile(0);
-  __syncthreads();
-  if (loader && ntiles > 1) issue_loads(1);
-  if (ntiles > 2) publish_offsets(2);
-  if (ntiles > 3) fetch_entry(3);
+  if (loader) {
+    if (ntiles > 1) issue_loads(1);
+    if (ntiles > 2) fetch_entries(2);
+  }
 
   // the q operands are redefined here by an empty asm: the waitcnt pass
   // would otherwise make the first MFMAs of every tile wait on the tile
@@ -239,7 +220,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
 
   const uint8_t* const k_rd = lds + q32 * K_ROW + hi * 16;
-  const uint8_t* const v_rd = lds + K_BYTES + q32 * V_ROW + hi * 16;
+  // transpose-read base: lane 4j+q of each 16-lane group addresses key row
+  // 4*hi + j (+8 for the second read, +16 per k-step) and channels
+  // 16*(group&1) + 4q .. +3 (+32 per channel block)
+  const int grp = lane >> 4;
+  const uint8_t* const v_rd =
+      lds + K_BYTES + (4 * hi + ((lane & 15) >> 2)) * V_ROW + (16 * (grp & 1) + 4 * (lane & 3)) * 2;
 
   for (int t = 0; t < ntiles; ++t) {
     const int n0 = t * BN;
@@ -249,7 +235,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       // ---- S^T = K Q^T: two 32-key blocks.  The K operands of block 1 are
       // read while block 0 multiplies, and the V^T operands of the first
       // channel block while block 1 does (the scheduling groups pin that
-      // order: LDS reads stay several MFMAs ahead of their use)
+      // order: LDS reads stay several MFMAs ahead of their use).  A V^T
+      // operand (channel block cb, k-step kk) is two transpose reads: keys
+      // 16kk + 4hi + 0..3 and 16kk + 8 + 4hi + 0..3 of the lane's channel.
       f32x16_t sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -257,6 +245,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
       bf16x8_t ka[KS];
       bf16x8_t va[4];
+      auto load_va = [&](int cb, int kk) {
+        const i16x4_t lo = lds_read_tr16(vt + kk * 16 * V_ROW + cb * 64);
+        const i16x4_t hi8 = lds_read_tr16(vt + (kk * 16 + 8) * V_ROW + cb * 64);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + ks * 32);
 #pragma unroll
@@ -267,7 +260,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[1], 0, 0, 0);
-        if (ks < 4) va[ks] = *reinterpret_cast<const bf16x8_t*>(vt + ks * 32);
+        if (ks < 4) va[ks] = load_va(0, ks);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
 #pragma unroll
@@ -278,7 +271,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       // ---- causal mask on tiles that cross a row's limit
       if (n0 + BN - 1 > wlim_lo) {
@@ -333,24 +326,24 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], pop[kk], o[cb], 0, 0, 0);
-          if (cb + 1 < CB)
-            va[kk] = *reinterpret_cast<const bf16x8_t*>(vt + (cb + 1) * 32 * V_ROW + kk * 32);
+          if (cb + 1 < CB) va[kk] = load_va(cb + 1, kk);
         }
       }
 #pragma unroll
       for (int i = 0; i < 4 * (CB - 1); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // tile t+1: registers -> the other stage; then tile t+2's loads, tile
-    // t+3's offsets and tile t+4's page entries go out
+    // tile t+1: registers -> the other stage; then tile t+2's loads and
+    // tile t+3's page entries go out
     if (loader && t + 1 < ntiles) store_tile((t + 1) & 1);
     __syncthreads();
-    if (loader && t + 2 < ntiles) issue_loads(t + 2);
-    if (t + 3 < ntiles) publish_offsets(t + 3);
-    if (t + 4 < ntiles) fetch_entry(t + 4);
+    if (loader) {
+      if (t + 2 < ntiles) issue_loads(t + 2);
+      if (t + 3 < ntiles) fetch_entries(t + 3);
+    }
   }
 
   // ---- normalise and write: lane holds channels 32cb + 8(e/4) + 4hi + e%4
