@@ -66,6 +66,9 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // Rows of the running maximum move only by more than this (log2 domain):
 // probabilities stay below 2^8, far inside bf16 / fp32 range.
 constexpr float kMaxSlack = 8.f;
+// A lane's row sum over one tile (32 probabilities) above this means some
+// probability may exceed 2^kMaxSlack.
+constexpr float kSumLimit = 256.f;
 
 template <int D, int WAVES>
 struct ExtendShape {
@@ -282,41 +285,59 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
           for (int e = 0; e < 16; ++e)
             if (32 * kb + 8 * (e >> 2) + (e & 3) > lim_rel) sc[kb][e] = -INFINITY;
       }
-      // ---- online softmax in the log2 domain: the scale (> 0) is applied
-      // to the row maximum and folded into one fma per score
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-      mx = xor32_max(mx) * p.scale_log2;
-      const bool move = mx > m_run + kMaxSlack;
-      const float mnew = move ? mx : m_run;
-      const float alpha = fast_exp2(m_run - mnew);
-      m_run = mnew;
+      // ---- online softmax in the log2 domain; the scale (> 0) is folded
+      // into one fma per score.  Fast path: exponentiate against the
+      // running maximum as it stands; that is exact softmax arithmetic as
+      // long as no probability exceeds 2^8, which a lane row sum of at most
+      // 2^8 guarantees.  Otherwise (and on a wave's first tile, whose
+      // maximum is still -inf) the tile maximum is taken, the running
+      // maximum moves if the tile's exceeds it by more than 2^8, and the
+      // probabilities are recomputed.
       float lsum = 0.f;
       bf16x8_t pop[4];
       constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+      auto probabilities = [&](float mref) {
+        lsum = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t wds[4];
+        for (int kk = 0; kk < 4; ++kk) {
+          uint32_t wds[4];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e = 8 * (kk & 1) + 2 * e2;
-          const float p0 = fast_exp2(fmaf(sc[kk >> 1][e], p.scale_log2, -mnew));
-          const float p1 = fast_exp2(fmaf(sc[kk >> 1][e + 1], p.scale_log2, -mnew));
-          wds[e2] = pack_bf16(p0, p1);
-          // the row sum adds the bf16 values that the P.V product uses
-          lsum = dot2_bf16(wds[e2], kOnes, lsum);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int e = 8 * (kk & 1) + 2 * e2;
+            const float p0 = fast_exp2(fmaf(sc[kk >> 1][e], p.scale_log2, -mref));
+            const float p1 = fast_exp2(fmaf(sc[kk >> 1][e + 1], p.scale_log2, -mref));
+            wds[e2] = pack_bf16(p0, p1);
+            // the row sum adds the bf16 values that the P.V product uses
+            lsum = dot2_bf16(wds[e2], kOnes, lsum);
+          }
+          pop[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
         }
-        pop[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
+      };
+      bool slow = m_run == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(slow) == 0) {
+        probabilities(m_run);
+        slow = !(lsum <= kSumLimit);  // also catches inf
       }
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        l_run *= alpha;
+      if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+        mx = xor32_max(mx) * p.scale_log2;
+        const bool move = mx > m_run + kMaxSlack;
+        const float mnew = move ? mx : m_run;
+        const float alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+        probabilities(m_run);
+        // the rescale is skipped when no row of the wave moved its maximum
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          l_run *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+        }
       }
       l_run += lsum;
       // ---- O^T += V^T P^T; the next channel block's operands are read one
