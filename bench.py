@@ -22,6 +22,7 @@ oracle timed on a bounded sample of the same workloads.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,39 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# HBM bytes per launch from two rocprofv3 --pmc runs of this benchmark
+# (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
+# for a plain 512 MiB device copy (x2 for FETCH_SIZE, x1 for WRITE_SIZE),
+# taken on the kernel sources with these SHA-256 digests.  When a source
+# has changed since, the figure no longer describes the kernel and is
+# reported as null.
+MEASURED_TRAFFIC = {
+    "decode": {  # decode_split_kernel + decode_merge_kernel
+        "sources": {"decode.hip": "85f498656a1b99faf34b00bc595c4d1aac0e57984c30db640c254a01214aacb7",
+                    "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
+        "bytes": 662458462,
+        "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
+    },
+    "extend": {
+        "sources": {"extend.hip": "cb653346044fc3adde38ea4b8c2ec912b047aa58a8e3e10666cce91d93c8a15c",
+                    "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
+        "bytes": 255799607,
+        "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
+    },
+}
+
+
+def measured_traffic(key):
+    ent = MEASURED_TRAFFIC.get(key)
+    if not ent or not ent["sources"] or ent["bytes"] is None:
+        return None
+    for rel, digest in ent["sources"].items():
+        path = os.path.join(ROOT, "paged_kv_attention_loc_amd", "csrc", rel)
+        with open(path, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return ent["bytes"]
 
 
 def log(msg):
@@ -304,7 +338,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode"),
             "algorithmic_bytes_per_launch": dbytes,
             "avg_launch_us": round(dec_ms * 1e3, 3),
             "median_launch_us": round(dec_med * 1e3, 3),
@@ -318,7 +352,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("extend"),
             "algorithmic_flops_per_launch": eflops,
             "avg_launch_us": round(ext_ms * 1e3, 3),
             "median_launch_us": round(ext_med * 1e3, 3),
