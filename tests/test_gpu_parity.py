@@ -255,6 +255,72 @@ def test_extend_sweep(d, G, ps):
     run_full(wl, f"extend d={d} G={G} ps={ps}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [2, 3, 16])
+@pytest.mark.parametrize("ps", [3, 13])
+def test_decode_sweep_uneven(d, G, ps):
+    # page sizes that are not powers of two (the division path of the slot
+    # formula) and group sizes the kernel pads up to 4 and 16 heads
+    hkv = 1 if G == 16 else 2
+    lens = [1, 5, 64, 255, 257, 600, 1029]
+    wl = build_case(500 + d + G + ps, num_qo_heads=hkv * G, num_kv_heads=hkv, head_dim=d,
+                    page_size=ps, prefix_lens=[l - 1 for l in lens], extend_lens=[1] * len(lens),
+                    kind="decode")
+    run_full(wl, f"decode d={d} G={G} ps={ps}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [2, 3, 16])
+@pytest.mark.parametrize("ps", [3, 13])
+def test_extend_sweep_uneven(d, G, ps):
+    hkv = 1 if G == 16 else 2
+    P = [0, 7, 100, 29]
+    E = [3, 70, 45, 130]
+    wl = build_case(600 + d + G + ps, num_qo_heads=hkv * G, num_kv_heads=hkv, head_dim=d,
+                    page_size=ps, prefix_lens=P, extend_lens=E, kind="extend")
+    run_full(wl, f"extend d={d} G={G} ps={ps}")
+
+
+@pytest.mark.parametrize("kind", ["decode", "extend"])
+def test_attention_with_strided_q(kind):
+    # q as the leading slice of a merged (T, Hq + 2 Hkv, d) projection
+    hq, hkv, d = 8, 2, 128
+    if kind == "decode":
+        wl = build_case(701, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=16,
+                        prefix_lens=[300, 40, 999], extend_lens=[1, 1, 1], kind="decode")
+    else:
+        wl = build_case(702, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=16,
+                        prefix_lens=[0, 130], extend_lens=[77, 260], kind="extend")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    T = ph.q.shape[0]
+    merged = torch.zeros((T, hq + 2 * hkv, d), dtype=torch.bfloat16)
+    merged[:, :hq] = ph.q
+    merged = merged.cuda()
+    q = merged[:, :hq]
+    assert q.stride(0) == (hq + 2 * hkv) * d
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    ti = _i32(ph.table_idx)
+    _say(f"strided q {kind}")
+    if kind == "decode":
+        out = msgl.paged_decode(dev.pool, 0, q, dev.pt, ti, _i32(ph.seq_lens), int(ph.seq_lens.max()))
+    else:
+        out = msgl.paged_extend(dev.pool, 0, q, dev.pt, ti, _i32(ph.prefix_lens), _i32(ph.extend_lens),
+                                _i32(ph.cu_extend_lens), int(ph.extend_lens.max()),
+                                int(ph.seq_lens.max()))
+    torch.cuda.synchronize()
+    _, ref = oracle_phase(bits(wl.pool), wl, ph)
+    assert_close(out, ref, what=f"strided q {kind}")
+
+
+def test_extend_four_wave_workgroups(monkeypatch):
+    # the 128-row workgroup variant selected by MSGL_EXTEND_WAVES=4
+    monkeypatch.setenv("MSGL_EXTEND_WAVES", "4")
+    wl = build_case(703, num_qo_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                    prefix_lens=[0, 300, 64], extend_lens=[200, 129, 1], kind="extend")
+    run_full(wl, "extend 4-wave workgroups")
+
+
 @pytest.mark.parametrize("E", [1, 2, 7, 31, 32, 33, 63, 64, 65])
 def test_extend_lengths(E):
     wl = build_case(400 + E, num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16,
