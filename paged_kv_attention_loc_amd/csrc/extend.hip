@@ -18,29 +18,33 @@
 //     kv heads every XCD (workgroups are dealt to the 8 XCDs round-robin)
 //     serves one kv head and keeps its K/V -- a shared prefix above all --
 //     in its own L2; the heaviest row tiles are launched first;
-//   * K/V tiles are double-buffered in LDS, one barrier per tile.  While
-//     tile t is computed, tile t+1 is in registers on its way to the other
-//     buffer and the page-table entries of tile t+2 are in flight;
-//   * every loading thread owns 4 consecutive keys and one 16-byte column,
-//     for K and for V alike; rows are read with buffer loads at 32-bit
-//     offsets inside the (K or V, layer) sub-tensor, whose range check
-//     also absorbs a wild page id;
+//   * K/V tiles are double-buffered in LDS, one barrier per tile.  The
+//     rows go from HBM straight into LDS (buffer_load ... lds, 16 bytes a
+//     lane, each wave instruction filling 1 KiB of consecutive LDS), issued
+//     by all waves one tile ahead, with no register staging; the page-table
+//     entries of the tile after are in flight meanwhile.  Rows are read at
+//     32-bit offsets inside the (K or V, layer) sub-tensor, whose range
+//     check also absorbs a wild page id;
 //   * each wave computes S^T = K Q^T, so a lane holds one query column and
 //     16 keys per 32-key block: the row maximum and sum need one exchange
 //     with the lane 32 apart (v_permlane32_swap);
-//   * K and V are both staged row-major.  The A operand of O^T = V^T P^T
-//     is read with two ds_read_b64_tr_b16 (the LDS transpose read of
-//     CDNA4: in each 16-lane group, lane i receives element i%4 of the
-//     8-byte pieces addressed by lanes 4j + i/4, j = 0..3), which turns
-//     four key rows into four keys of one channel per lane, in the order
-//     in which the S^T accumulator registers hold the keys -- so P^T feeds
-//     the second MFMA straight from registers.  K rows are padded by 16
-//     bytes and V rows by 64: with 64 four-byte banks every 16-lane read
-//     and write hits distinct banks, and every LDS address is a per-lane
-//     base plus a compile-time offset;
+//   * K and V are both staged row-major, unpadded, with the 16-byte
+//     columns of each row XOR-permuted: the DMA fetches, for each LDS
+//     slot, the column that the permutation puts there.  K reads (one
+//     16-byte operand per lane and k-step) then hit distinct banks within
+//     every 16-lane group, and so do the V reads: the A operand of O^T =
+//     V^T P^T is two ds_read_b64_tr_b16 (the LDS transpose read of CDNA4:
+//     in each 16-lane group, lane i receives element i%4 of the 8-byte
+//     pieces addressed by lanes 4j + i/4, j = 0..3), which turns four key
+//     rows into four keys of one channel per lane, in the order in which
+//     the S^T accumulator registers hold the keys -- so P^T feeds the
+//     second MFMA straight from registers.  Per-lane read addresses are
+//     computed once; the tile, stage and block parts are immediates;
 //   * the running maximum only moves when a row's new maximum exceeds it by
 //     more than 2^8 in exp2 terms, so the O rescale is rare; masking runs
 //     only on tiles that cross a row's causal limit.
+#include <type_traits>
+
 #include "common.h"
 
 namespace msgl {
@@ -54,6 +58,14 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4_t*)(__attribute__((address_space(3))) const uint8_t*)(addr));
+}
+
+// 16 bytes per lane from the buffer at byte offset `off` straight into LDS:
+// lane i writes lds_base + 16*i (one 1 KiB run per wave instruction)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)(__attribute__((address_space(3))) uint8_t*)lds_base,
+      16, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t extend_rsrc(const void* base, uint32_t bytes) {
@@ -74,18 +86,31 @@ template <int D, int WAVES>
 struct ExtendShape {
   static constexpr int BM = 32 * WAVES;   // packed rows per workgroup
   static constexpr int BN = 64;           // keys per tile
-  static constexpr int NCOL = D / 8;      // 16-byte columns per K/V row
   static constexpr int KS = D / 16;       // MFMA k-steps of Q.K^T
   static constexpr int CB = D / 32;       // 32-channel blocks of the output
-  static constexpr int K_ROW = D * 2 + 16;   // bytes per staged K row
-  static constexpr int V_ROW = D * 2 + 64;   // bytes per staged V row
-  static constexpr int K_BYTES = BN * K_ROW;
-  static constexpr int V_BYTES = BN * V_ROW;
-  static constexpr int BUF = K_BYTES + V_BYTES;   // one pipeline stage
-  static constexpr int LOADERS = (BN / 4) * NCOL;  // threads that load a tile
-  static_assert(LOADERS <= 64 * WAVES, "not enough threads to load a tile");
-  static_assert(BN <= 64 * WAVES, "one thread per key computes row offsets");
+  static constexpr int ROWB = D * 2;      // bytes per staged K or V row
+  static constexpr int SPR = ROWB / 16;   // 16-byte slots per row
+  static constexpr int K_BYTES = BN * ROWB;
+  static constexpr int STAGE = 2 * K_BYTES;        // K then V of one tile
+  static constexpr int RPI = 1024 / ROWB;          // rows per DMA instruction
+  static constexpr int NINST = BN / RPI;           // DMA instructions per tile and matrix
+  static constexpr int IPW = NINST / WAVES;        // ... per wave
+  static_assert(IPW >= 1 && IPW * WAVES == NINST, "DMA instructions must split evenly");
 };
+
+// XOR permutation of the 16-byte slots of staged row `row` (0..63 of a
+// tile).  K: 16 lanes reading 16 consecutive rows at one logical slot hit
+// 16 distinct bank groups.  V: the 32 lanes of one transpose-read pass
+// (rows 4hi + j, j = 0..3, slots of two channel halves) hit 64 distinct
+// banks.  Both depend only on row bits that are fixed for a lane.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 }  // namespace
 
@@ -93,8 +118,9 @@ template <int D, bool POW2, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
                                                                const int32_t* __restrict__ page_table) {
   using S = ExtendShape<D, WAVES>;
-  constexpr int BM = S::BM, BN = S::BN, NCOL = S::NCOL, KS = S::KS, CB = S::CB;
-  constexpr int K_ROW = S::K_ROW, V_ROW = S::V_ROW, K_BYTES = S::K_BYTES, BUF = S::BUF;
+  constexpr int BM = S::BM, BN = S::BN, KS = S::KS, CB = S::CB;
+  constexpr int ROWB = S::ROWB, SPR = S::SPR, K_BYTES = S::K_BYTES, STAGE = S::STAGE;
+  constexpr int RPI = S::RPI, IPW = S::IPW;
 
   const int g = blockIdx.x;
   const int r = blockIdx.y;
@@ -114,7 +140,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const int hi = lane >> 5;
   const int Hq = p.num_kv_heads * G;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
 
   // this lane's query row (rows past the end are clamped and not written)
   const int mrow = m0 + w * 32 + q32;
@@ -147,50 +173,32 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const __amdgpu_buffer_rsrc_t vrs =
       extend_rsrc(p.v_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
 
-  // loader role: keys 4kq .. 4kq+3 of a tile, 16-byte column cg, for K and
-  // V alike.  Its page entries are fetched a tile ahead of the row loads;
-  // keys past kv_end are clamped to the last key, whose row is valid
-  // (those keys are masked for every row).
-  const bool loader = tid < S::LOADERS;
-  const int kq = tid / NCOL;
-  const int cg = tid % NCOL;
-  // with a power-of-two page size of at least 4 the four keys share a page
-  const bool one_page = POW2 && ps >= 4;
-  int ent[4];
-  auto tile_key = [&](int t, int j) { return min(t * BN + 4 * kq + j, kv_end - 1); };
+  // DMA role, all waves: wave w fills rows RPI*i .. RPI*i+RPI-1 of the K
+  // and V tiles for i = w*IPW .. w*IPW+IPW-1; lane l fetches LDS slot
+  // l % SPR of row RPI*i + l / SPR, i.e. the row's column slot ^ swz(row).
+  // Its page entry is fetched a tile ahead; keys past kv_end are clamped
+  // to the last key, whose row is valid (they are masked for every row).
+  int ent[IPW];
+  auto dma_row = [&](int k) { return RPI * (w * IPW + k) + lane / SPR; };
+  auto dma_key = [&](int t, int k) { return min(t * BN + dma_row(k), kv_end - 1); };
   auto fetch_entries = [&](int t) {
-    if (one_page) {
-      ent[0] = pt[tile_key(t, 0) >> sh];
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = tile_key(t, j);
-        ent[j] = POW2 ? pt[key >> sh] : pt[key / ps];
-      }
+    for (int k = 0; k < IPW; ++k) {
+      const int key = dma_key(t, k);
+      ent[k] = POW2 ? pt[key >> sh] : pt[key / ps];
     }
   };
-  uint4 kr[4], vr[4];
-  auto issue_loads = [&](int t) {  // tile t's rows, using the entries in ent
+  auto issue_dma = [&](int t, int stage) {  // tile t into stage, from the entries in ent
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = tile_key(t, j);
-      const int e = one_page ? ent[0] : ent[j];
-      const int slot = POW2 ? (e << sh) + (key & (ps - 1)) : e * ps + key % ps;
-      const uint32_t off = static_cast<uint32_t>(slot) * row_bytes + cg * 16;
-      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-      const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-      kr[j] = make_uint4(a.x, a.y, a.z, a.w);
-      vr[j] = make_uint4(b.x, b.y, b.z, b.w);
-    }
-  };
-  // registers -> LDS stage b: K and V rows
-  uint8_t* const k_st = lds + kq * 4 * K_ROW + cg * 16;
-  uint8_t* const v_st = lds + K_BYTES + kq * 4 * V_ROW + cg * 16;
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4*>(k_st + b * BUF + j * K_ROW) = kr[j];
-      *reinterpret_cast<uint4*>(v_st + b * BUF + j * V_ROW) = vr[j];
+    for (int k = 0; k < IPW; ++k) {
+      const int row = dma_row(k);
+      const int key = dma_key(t, k);
+      const int slot = POW2 ? (ent[k] << sh) + (key & (ps - 1)) : ent[k] * ps + key % ps;
+      const uint32_t base = static_cast<uint32_t>(slot) * row_bytes;
+      const int sl = lane % SPR;
+      const int i = w * IPW + k;
+      dma16(krs, lds + stage * STAGE + i * 1024, base + (sl ^ swz_k<D>(row)) * 16);
+      dma16(vrs, lds + stage * STAGE + K_BYTES + i * 1024, base + (sl ^ swz_v<D>(row)) * 16);
     }
   };
 
@@ -202,19 +210,14 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // prologue: tile 0 staged, tile 1 in registers, tile 2's entries in
-  // flight
-  if (loader) {
-    fetch_entries(0);
-    issue_loads(0);
-    if (ntiles > 1) fetch_entries(1);
-    store_tile(0);
-  }
+  // prologue: tile 0 in stage 0; tile 1 on its way to stage 1; tile 2's
+  // entries in flight (the barrier's fence waits for the DMA)
+  fetch_entries(0);
+  issue_dma(0, 0);
+  if (ntiles > 1) fetch_entries(1);
   __syncthreads();
-  if (loader) {
-    if (ntiles > 1) issue_loads(1);
-    if (ntiles > 2) fetch_entries(2);
-  }
+  if (ntiles > 1) issue_dma(1, 1);
+  if (ntiles > 2) fetch_entries(2);
 
   // the q operands are redefined here by an empty asm: the waitcnt pass
   // would otherwise make the first MFMAs of every tile wait on the tile
@@ -222,19 +225,32 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
 
-  const uint8_t* const k_rd = lds + q32 * K_ROW + hi * 16;
-  // transpose-read base: lane 4j+q of each 16-lane group addresses key row
-  // 4*hi + j (+8 for the second read, +16 per k-step) and channels
-  // 16*(group&1) + 4q .. +3 (+32 per channel block)
-  const int grp = lane >> 4;
-  const uint8_t* const v_rd =
-      lds + K_BYTES + (4 * hi + ((lane & 15) >> 2)) * V_ROW + (16 * (grp & 1) + 4 * (lane & 3)) * 2;
+  // per-lane LDS read offsets.  K operand (k-step ks): row q32 (+32 per
+  // key block), logical slot 2ks + hi.  V operand (channel block cb):
+  // lane 4j+q of each 16-lane group reads key row 4*hi + j (+8 for the
+  // second read, +16 per k-step) at channels 16*(group&1) + 4q .. +3 of
+  // the block, an 8-byte half of one slot.
+  uint32_t kofs[KS], vofs[CB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = q32 * ROWB + ((2 * ks + hi) ^ swz_k<D>(q32)) * 16;
+  {
+    const int j = (lane & 15) >> 2, q = lane & 3, grp = lane >> 4;
+    const int vrow = 4 * hi + j;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int logical = 4 * cb + 2 * (grp & 1) + (q >> 1);
+      vofs[cb] = K_BYTES + vrow * ROWB + (logical ^ swz_v<D>(vrow)) * 16 + 8 * (q & 1);
+    }
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
+  // one tile; ST (compile time) is its stage, so that stage offsets are
+  // immediates of the LDS reads
+  auto tile = [&](int t, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
     const int n0 = t * BN;
     if (wave_rows && n0 <= wlim_hi) {
-      const uint8_t* kt = k_rd + (t & 1) * BUF;
-      const uint8_t* vt = v_rd + (t & 1) * BUF;
+      const uint8_t* kt = lds + ST * STAGE;
+      const uint8_t* vt = lds + ST * STAGE;
       // ---- S^T = K Q^T: two 32-key blocks.  The K operands of block 1 are
       // read while block 0 multiplies, and the V^T operands of the first
       // channel block while block 1 does (the scheduling groups pin that
@@ -249,16 +265,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       bf16x8_t ka[KS];
       bf16x8_t va[4];
       auto load_va = [&](int cb, int kk) {
-        const i16x4_t lo = lds_read_tr16(vt + kk * 16 * V_ROW + cb * 64);
-        const i16x4_t hi8 = lds_read_tr16(vt + (kk * 16 + 8) * V_ROW + cb * 64);
+        const i16x4_t lo = lds_read_tr16(vt + vofs[cb] + kk * 16 * ROWB);
+        const i16x4_t hi8 = lds_read_tr16(vt + vofs[cb] + (kk * 16 + 8) * ROWB);
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7));
       };
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + ks * 32);
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[0], 0, 0, 0);
-        ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + 32 * K_ROW + ks * 32);
+        ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks] + 32 * ROWB);
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -357,14 +373,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // tile t+1: registers -> the other stage; then tile t+2's loads and
-    // tile t+3's page entries go out
-    if (loader && t + 1 < ntiles) store_tile((t + 1) & 1);
+    // every wave is done with this stage and tile t+1 has landed in the
+    // other one (vmcnt(0): the DMA is a vector-memory operation); then
+    // tile t+2 goes into this stage and tile t+3's page entries go out
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (loader) {
-      if (t + 2 < ntiles) issue_loads(t + 2);
-      if (t + 3 < ntiles) fetch_entries(t + 3);
-    }
+    if (t + 2 < ntiles) issue_dma(t + 2, ST);
+    if (t + 3 < ntiles) fetch_entries(t + 3);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and write: lane holds channels 32cb + 8(e/4) + 4hi + e%4
