@@ -49,13 +49,13 @@ MEASURED_TRAFFIC = {
     "decode": {  # decode_split_kernel + decode_merge_kernel
         "sources": {"decode.hip": "85f498656a1b99faf34b00bc595c4d1aac0e57984c30db640c254a01214aacb7",
                     "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
-        "bytes": 662458462,
+        "bytes": 662501464,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
-        "sources": {"extend.hip": "cb653346044fc3adde38ea4b8c2ec912b047aa58a8e3e10666cce91d93c8a15c",
+        "sources": {"extend.hip": "d705a03e97f4a81edfb03b7e2ac66a9a9fe75379c267c8aa7eff29aee7cac375",
                     "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
-        "bytes": 255799607,
+        "bytes": 245847608,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
 }
