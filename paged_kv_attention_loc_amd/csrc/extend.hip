@@ -386,20 +386,43 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
     if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- normalise and write: lane holds channels 32cb + 8(e/4) + 4hi + e%4
-  const float l_tot = xor32_sum(l_run);
-  if (mrow < M) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = p.out + (static_cast<int64_t>(p.cu_extend[r] + ti) * Hq + g * G + hh) * D;
+  // ---- normalise; the lane holds channels 32cb + 8(e/4) + 4hi + e%4 of
+  // its row.  The wave's 32 rows are staged in LDS (16-byte slots
+  // XOR-permuted by row, so that the 8-byte writes and the 16-byte reads
+  // spread over the banks) and stored as whole rows, 16 bytes a lane, so
+  // that each store instruction covers full cache lines.  The stores are
+  // nontemporal: nothing here reads the output again, and streaming it out
+  // now keeps dirty lines from being written back later, in the middle of
+  // whatever runs next.  Every wave has passed the loop's last barrier, so
+  // the stages are free.
+  static_assert(WAVES * 32 * ROWB <= 2 * STAGE, "output staging must fit in the stages");
+  {
+    const float inv = 1.f / xor32_sum(l_run);
+    uint8_t* ow = lds + w * 32 * ROWB;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int ch = 32 * cb + 8 * e4 + 4 * hi;
+        const int slot = 4 * cb + e4;  // channels 8*slot .. 8*slot+7
         uint2 wv;
         wv.x = pack_bf16(o[cb][4 * e4 + 0] * inv, o[cb][4 * e4 + 1] * inv);
         wv.y = pack_bf16(o[cb][4 * e4 + 2] * inv, o[cb][4 * e4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + ch) = wv;
+        *reinterpret_cast<uint2*>(ow + q32 * ROWB + (slot ^ (q32 & (SPR - 1))) * 16 + 8 * hi) = wv;
+      }
+    }
+    __syncthreads();
+    constexpr int RPS = 64 / SPR;  // rows per store instruction
+    const int k = lane % SPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPS; ++i) {
+      const int rr = i * RPS + lane / SPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ow + rr * ROWB + (k ^ (rr & (SPR - 1))) * 16);
+      const int orow_m = m0 + w * 32 + rr;
+      if (orow_m < M) {
+        const int oti = orow_m / G;
+        const int ohh = orow_m - oti * G;
+        uint16_t* dst = p.out + (static_cast<int64_t>(p.cu_extend[r] + oti) * Hq + g * G + ohh) * D + k * 8;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
       }
     }
   }
