@@ -14,6 +14,7 @@
 // arithmetic; chunks are short (256 tokens by default) so that many
 // independent waves are in flight while the split partials stay a few
 // percent of the KV bytes.
+//   * the K/V loads carry the nontemporal hint: every byte is read once;
 //   * addressing: one vector load per tile fetches the tile's page ids
 //     (lane t: token t), one tile ahead; each token's row byte offset is
 //     then moved into an SGPR (v_readlane) and every K/V load is a buffer
@@ -56,6 +57,12 @@ template <int GM>
 struct DecodeOccupancy {
   static constexpr int value = GM <= 8 ? 4 : 2;
 };
+
+// Cache policy of the K/V loads: nontemporal (the nt bit of the buffer
+// load).  Each K/V byte is read exactly once per launch, so the stream is
+// marked as such and does not displace what the caches hold for the
+// kernels around it; measured, the decode itself also runs faster so.
+constexpr int kStream = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   // dword 3 = 0x00020000: 32-bit data format, raw (unswizzled) addressing
@@ -152,10 +159,10 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
     uint32_t kw[TILE], vw[TILE];
 #pragma unroll
     for (int t = 0; t < TILE; ++t)
-      kw[t] = __builtin_amdgcn_raw_buffer_load_b32(krs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), 0);
+      kw[t] = __builtin_amdgcn_raw_buffer_load_b32(krs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), kStream);
 #pragma unroll
     for (int t = 0; t < TILE; ++t)
-      vw[t] = __builtin_amdgcn_raw_buffer_load_b32(vrs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), 0);
+      vw[t] = __builtin_amdgcn_raw_buffer_load_b32(vrs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), kStream);
     if (lane < CPL) {
 #pragma unroll
       for (int t = 0; t < TILE; ++t) k_words[t * KROW + cw] = kw[t];

@@ -50,7 +50,16 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
                          static_cast<int64_t>(piece) * VEC;
     uint8_t* dst = (half ? p.v_cache : p.k_cache) + static_cast<int64_t>(slot) * p.row_bytes +
                    static_cast<int64_t>(piece) * VEC;
-    *reinterpret_cast<V*>(dst) = *reinterpret_cast<const V*>(src);
+    if constexpr (VEC == 16) {
+      // nontemporal on both sides: the new rows are read once here, and
+      // written through rather than left as dirty lines that a later,
+      // bandwidth-bound kernel would have to write back
+      typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src)),
+                                  reinterpret_cast<u32x4v*>(dst));
+    } else {
+      *reinterpret_cast<V*>(dst) = *reinterpret_cast<const V*>(src);
+    }
   }
 }
 
