@@ -172,6 +172,50 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
                               void* stream);
 
 /*
+ * Decode graphs: store_kv of one new row per request followed by
+ * paged_decode, captured once into a HIP graph for a fixed (padded) batch
+ * size and replayed with one launch ("Code Notes: mini-sglang", Engine
+ * Layer table, GraphRunner row -- decode batches are replayed from graphs
+ * captured at fixed batch sizes to hide launch overhead).
+ *
+ * msgl_decode_graph_create captures, on a private stream of its own:
+ *     msgl_store_kv(pool, layer, k, k_row_stride, v, v_row_stride, out_loc, batch)
+ *     msgl_paged_decode(pool, layer, q, q_row_stride, out, page_table, ..., batch, ...)
+ * with the arguments' meaning, layout and validation exactly as for those
+ * two calls (every scalar and pointer is checked before capture begins).
+ * The pointers are baked into the graph: the buffers they name are the
+ * graph's static inputs and outputs, which the caller refills before each
+ * launch and must keep allocated until the graph is destroyed.  Rows of a
+ * smaller real batch are padded with out_loc = -1 and seq_lens = 0 (zeros
+ * out, no KV read).  max_seq_len is the bound the grid is sized for; every
+ * replayed seq_lens[r] must stay within it.
+ *   graph_out : receives the new graph (host object owning a HIP graph
+ *               executable; no device buffer is allocated by the library).
+ * Returns MSGL_ERR_UNSUPPORTED in checked mode (MSGL_CHECK=1), whose host
+ * synchronisation cannot be captured, and MSGL_ERR_HIP when capture or
+ * instantiation fails; *graph_out is then NULL.
+ *
+ * msgl_decode_graph_launch replays the graph on `stream` (asynchronous,
+ * ordered like any other call on that stream).  Launches of one graph
+ * share its workspace and static buffers: they must not overlap in time.
+ * msgl_decode_graph_destroy releases it (NULL is a no-op); the caller
+ * makes sure no launch of it is still pending.
+ */
+typedef struct msgl_decode_graph msgl_decode_graph;
+
+msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, const void* k,
+                                     int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                     const int32_t* out_loc, const void* q, int64_t q_row_stride,
+                                     void* out, const int32_t* page_table,
+                                     int32_t page_table_stride, const int32_t* table_idx,
+                                     const int32_t* seq_lens, int32_t batch,
+                                     int32_t num_qo_heads, int32_t max_seq_len, float sm_scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     msgl_decode_graph** graph_out);
+msgl_status msgl_decode_graph_launch(const msgl_decode_graph* graph, void* stream);
+msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph);
+
+/*
  * debug_gather_kv (for tests): copy tokens 0 .. len-1 of page_table row
  * `row` out of the pool in logical order -- the page-table address
  * translation the attention kernels use, exposed on its own.

@@ -37,6 +37,7 @@ __all__ = [
     "paged_decode_workspace_size",
     "paged_extend",
     "debug_gather_kv",
+    "DecodeGraph",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +95,13 @@ def load_library():
                                       F32, P]
     lib.msgl_debug_gather_kv.restype = I32
     lib.msgl_debug_gather_kv.argtypes = [PP, I32, P, I32, I32, I32, P, P, P]
+    lib.msgl_decode_graph_create.restype = I32
+    lib.msgl_decode_graph_create.argtypes = [PP, I32, P, I64, P, I64, P, P, I64, P, P, I32, P, P, I32,
+                                             I32, I32, F32, P, SZ, ctypes.POINTER(P)]
+    lib.msgl_decode_graph_launch.restype = I32
+    lib.msgl_decode_graph_launch.argtypes = [P, P]
+    lib.msgl_decode_graph_destroy.restype = I32
+    lib.msgl_decode_graph_destroy.argtypes = [P]
     _lib = lib
     return lib
 
@@ -227,6 +235,99 @@ def msgl_debug_gather_kv(pool: torch.Tensor, layer: int, page_table: torch.Tenso
                                              v.data_ptr(), _stream(pool))
     _check(st, "msgl_debug_gather_kv")
     return k, v
+
+
+class DecodeGraph:
+    """store_kv of one new K/V row per request + paged decode, captured once
+    for a fixed padded batch and replayed with a single graph launch
+    (``msgl_decode_graph_*``; "Code Notes: mini-sglang", Engine Layer
+    table, GraphRunner row).
+
+    The graph reads and writes static tensors owned by this object; ``run``
+    copies a real batch of ``b <= batch`` rows into them, pads the rest
+    (out_loc -1, seq_lens 0, table_idx 0: no store, zero output, no KV read)
+    and launches on the current stream.  ``page_table`` is referenced, not
+    copied: the caller keeps it allocated and updates it in place.  One
+    graph's launches share its buffers, so they are stream-ordered here.
+    """
+
+    def __init__(self, pool: torch.Tensor, layer: int, batch: int, num_qo_heads: int,
+                 max_seq_len: int, page_table: torch.Tensor, sm_scale: Optional[float] = None):
+        ps = _pool_struct(pool)
+        if page_table.dim() != 2:
+            raise ValueError("page_table must be 2-D (rows, entries)")
+        dev = pool.device
+        d, hkv = ps.head_dim, ps.num_kv_heads
+        self.batch, self.max_seq_len = int(batch), int(max_seq_len)
+        self.pool, self.page_table = pool, page_table
+        self.q = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
+        self.k = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
+        self.out = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
+        self.out_loc = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+        self.table_idx = torch.zeros((batch,), dtype=torch.int32, device=dev)
+        self.seq_lens = torch.zeros((batch,), dtype=torch.int32, device=dev)
+        need = msgl_paged_decode_workspace_size(batch, num_qo_heads, hkv, d, max_seq_len)
+        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(d)
+        self._pool_struct = ps
+        handle = ctypes.c_void_p()
+        torch.cuda.synchronize(dev)  # the static tensors above are initialised
+        lib = load_library()
+        st = lib.msgl_decode_graph_create(
+            ctypes.byref(ps), layer, self.k.data_ptr(), hkv * d, self.v.data_ptr(), hkv * d,
+            self.out_loc.data_ptr(), self.q.data_ptr(), num_qo_heads * d, self.out.data_ptr(),
+            _i32(page_table, "page_table"), int(page_table.shape[1]), self.table_idx.data_ptr(),
+            self.seq_lens.data_ptr(), batch, num_qo_heads, int(max_seq_len), float(sm_scale),
+            self.workspace.data_ptr(), self.workspace.numel(), ctypes.byref(handle))
+        _check(st, "msgl_decode_graph_create")
+        self._handle = handle
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out_loc: torch.Tensor,
+            table_idx: torch.Tensor, seq_lens: torch.Tensor) -> torch.Tensor:
+        """Store k/v rows at out_loc and decode q; returns out[:b] (a view of
+        the static output, overwritten by the next run)."""
+        b = int(q.shape[0])
+        if b < 1 or b > self.batch:
+            raise ValueError(f"batch {b} outside 1..{self.batch}")
+        for name, t, shape in (("q", q, self.q.shape[1:]), ("k", k, self.k.shape[1:]),
+                               ("v", v, self.v.shape[1:])):
+            if t.shape[0] != b or tuple(t.shape[1:]) != tuple(shape) or t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be bf16 shaped ({b}, {tuple(shape)})")
+        for name, t in (("out_loc", out_loc), ("table_idx", table_idx), ("seq_lens", seq_lens)):
+            if t.numel() != b or t.dtype != torch.int32:
+                raise ValueError(f"{name} must be {b} int32 values")
+        self.q[:b].copy_(q)
+        self.k[:b].copy_(k)
+        self.v[:b].copy_(v)
+        self.out_loc[:b].copy_(out_loc)
+        self.table_idx[:b].copy_(table_idx)
+        self.seq_lens[:b].copy_(seq_lens)
+        if b < self.batch:
+            self.out_loc[b:].fill_(-1)
+            self.table_idx[b:].fill_(0)
+            self.seq_lens[b:].fill_(0)
+        self.launch()
+        return self.out[:b]
+
+    def launch(self) -> None:
+        """Replay the graph on the current stream over the static buffers as
+        they stand."""
+        st = load_library().msgl_decode_graph_launch(self._handle, _stream(self.q))
+        _check(st, "msgl_decode_graph_launch")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            torch.cuda.synchronize(self.q.device)
+            load_library().msgl_decode_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # short names

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "msgl.h"
@@ -82,13 +83,9 @@ msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_he
 }
 
 // Decode workspace layout: fp32 partial outputs (batch, max_chunks, Hq, d),
-// then their (max, sum) pairs, 256-byte aligned.
-// Tokens per decode split: a multiple of 64 (MSGL_DECODE_SPLIT overrides
-// the default of 64 -- short splits keep many independent waves in flight,
-// which measured faster than longer ones despite the extra partials),
-// doubled until no request can need more than
-// kMaxDecodeSplits splits -- the merge kernel keeps one weight per split in
-// LDS.
+// then their (max, sum) pairs, 256-byte aligned.  The split size (see
+// decode_chunk) is doubled until no request needs more than
+// kMaxDecodeSplits splits.
 constexpr int64_t kMaxDecodeSplits = 4096;
 // Waves per extend workgroup (32 query rows each): 8 by default;
 // MSGL_EXTEND_WAVES=4 selects 128-row workgroups.
@@ -133,6 +130,11 @@ msgl_status check_row_pages(const int32_t* page_table, int64_t stride, int32_t r
 }
 
 }  // namespace
+
+// A captured store_kv + decode: the instantiated HIP graph.
+struct msgl_decode_graph {
+  hipGraphExec_t exec;
+};
 
 extern "C" {
 
@@ -405,6 +407,73 @@ msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.num_items = static_cast<int64_t>(len) * 2 * p.pieces_per_row;
   return hip_status(launch_gather(p, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, const void* k,
+                                     int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                     const int32_t* out_loc, const void* q, int64_t q_row_stride,
+                                     void* out, const int32_t* page_table,
+                                     int32_t page_table_stride, const int32_t* table_idx,
+                                     const int32_t* seq_lens, int32_t batch,
+                                     int32_t num_qo_heads, int32_t max_seq_len, float sm_scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     msgl_decode_graph** graph_out) {
+  if (!graph_out) return MSGL_ERR_NULL;
+  *graph_out = nullptr;
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (batch < 1) return MSGL_ERR_SHAPE;
+  // checked mode copies device data to the host: not capturable
+  if (env_on("MSGL_CHECK")) return MSGL_ERR_UNSUPPORTED;
+  // the device query is made (and cached) outside the capture
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MSGL_ERR_HIP;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    hipStreamDestroy(cs);
+    return MSGL_ERR_HIP;
+  }
+  // the two calls validate every argument before they launch anything; a
+  // validation error still ends the capture below
+  st = msgl_store_kv(pool, layer, k, k_row_stride, v, v_row_stride, out_loc, batch, cs);
+  if (st == MSGL_OK)
+    st = msgl_paged_decode(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                           table_idx, seq_lens, batch, num_qo_heads, max_seq_len, sm_scale,
+                           workspace, workspace_bytes, cs);
+  hipGraph_t graph = nullptr;
+  const hipError_t end = hipStreamEndCapture(cs, &graph);
+  hipGraphExec_t exec = nullptr;
+  if (st == MSGL_OK && end == hipSuccess && graph)
+    st = hip_status(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+  else if (st == MSGL_OK)
+    st = MSGL_ERR_HIP;
+  if (graph) hipGraphDestroy(graph);
+  hipStreamDestroy(cs);
+  if (st != MSGL_OK) {
+    if (exec) hipGraphExecDestroy(exec);
+    return st;
+  }
+  msgl_decode_graph* g = new (std::nothrow) msgl_decode_graph;
+  if (!g) {
+    hipGraphExecDestroy(exec);
+    return MSGL_ERR_HIP;
+  }
+  g->exec = exec;
+  *graph_out = g;
+  return MSGL_OK;
+}
+
+msgl_status msgl_decode_graph_launch(const msgl_decode_graph* graph, void* stream) {
+  if (!graph || !graph->exec) return MSGL_ERR_NULL;
+  return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph) {
+  if (!graph) return MSGL_OK;
+  const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+  delete graph;
+  return hip_status(e);
 }
 
 }  // extern "C"
