@@ -202,6 +202,73 @@ def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
     }
 
 
+def graph_vs_eager(msgl, dev, iters=300):
+    """A small decode step -- store_kv of 8 new rows, then decode of 8
+    requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
+    calls and as one launch of a captured decode graph, back to back with
+    one synchronisation at the end (launch overhead dominates at this size)."""
+    from workloads import build_case
+    B, L = 8, 512
+    wl = build_case(8, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    prefix_lens=[L - 1] * B, extend_lens=[1] * B, num_pages=4096, device=dev)
+    ph = wl.phases[0]
+    p = Prepared(wl, ph, dev)
+    g = msgl.DecodeGraph(p.pool, wl.layer, B, wl.num_qo_heads, L, p.pt)
+    g.q.copy_(p.q)
+    g.k.copy_(p.k)
+    g.v.copy_(p.v)
+    g.out_loc.copy_(p.loc)
+    g.table_idx.copy_(p.ti)
+    g.seq_lens.copy_(p.sl)
+
+    def eager():
+        run_store(msgl, p)
+        run_decode(msgl, p)
+
+    res = {"batch": B, "seq_len": L}
+    for name, fn in (("eager", eager), ("graph", g.launch)):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            fn()
+        torch.cuda.synchronize()
+        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / iters * 1e6, 2)
+    res["graph_matches_eager"] = bool(torch.equal(g.out.view(torch.int16), p.out.view(torch.int16)))
+    g.close()
+
+    # a whole decode step over NL layers (store_kv + decode per layer, the
+    # same calls), eager against one replay of a torch graph capturing them
+    NL = 32
+    pool = torch.randn((2, NL) + tuple(wl.pool.shape[2:]), device=dev).to(torch.bfloat16)
+    out = torch.empty_like(p.q)
+
+    def layers():
+        for layer in range(NL):
+            msgl.store_kv(pool, layer, p.k, p.v, p.loc)
+            msgl.paged_decode(pool, layer, p.q, p.pt, p.ti, p.sl, p.max_len, out=out,
+                              workspace=p.ws)
+
+    layers()
+    torch.cuda.synchronize()
+    tg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(tg):
+        layers()
+    res["layers"] = NL
+    for name, fn in (("eager_layers", layers), ("graph_layers", tg.replay)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters // 10):
+            fn()
+        torch.cuda.synchronize()
+        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / (iters // 10) * 1e6, 1)
+    del tg, pool
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +367,9 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
+    log("decode graph vs eager calls (small batch)")
+    graph_stats = graph_vs_eager(msgl, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl_dec, ph_d, wl_ext, ph_e, args.cpu_budget)
@@ -366,6 +436,7 @@ def main():
             "extend_GBs": round(sb_ext / (st_ext_ms * 1e-3) / 1e9, 2),
         },
         "extend_tflops": round(ext_tflops, 2),
+        "decode_graph": graph_stats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -127,3 +127,48 @@ def test_decode_graph_rejects_bad_arguments():
         msgl.DecodeGraph(pool, 0, 4, 7, 64, pt)  # 7 q heads over 2 kv heads
     with pytest.raises(msgl.MsglError):
         msgl.DecodeGraph(pool, 0, 4, 8, 16 * 9, pt)  # max_seq_len beyond the table width
+
+
+def test_eager_calls_capture_in_a_torch_graph_over_layers():
+    # the eager calls are capturable as they are: several layers of store_kv
+    # + decode in one torch graph, replayed with fresh inputs, equal the
+    # eager calls bit for bit
+    ps, hq, hkv, d, cap, B, NL = 16, 8, 2, 128, 400, 4, 3
+    wl = build_case(331, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=[cap - 1] * B, extend_lens=[1] * B)
+    ph = wl.phases[0]
+    gen = torch.Generator().manual_seed(5)
+    pool = torch.randn((2, NL) + tuple(wl.pool.shape[2:]), generator=gen).to(torch.bfloat16).cuda()
+    pool_e = pool.clone()
+    pt = torch.from_numpy(wl.page_table).cuda()
+    loc, ti, sl = _i32(ph.out_loc), _i32(ph.table_idx), _i32(ph.seq_lens)
+    q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((B, hkv, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    ws = torch.empty(msgl.paged_decode_workspace_size(B, hq, hkv, d, cap), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(NL)]
+
+    def step(pl, o):
+        for layer in range(NL):
+            msgl.store_kv(pl, layer, k, v, loc)
+            msgl.paged_decode(pl, layer, q, pt, ti, sl, cap, out=o[layer], workspace=ws)
+
+    step(pool, outs)  # warm up outside the capture
+    torch.cuda.synchronize()
+    tg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(tg):
+        step(pool, outs)
+    step(pool_e, [torch.empty_like(o) for o in outs])  # keep the two pools in step
+    for it in range(3):
+        q.copy_(torch.randn((B, hq, d), generator=gen).to(torch.bfloat16))
+        k.copy_(torch.randn((B, hkv, d), generator=gen).to(torch.bfloat16))
+        v.copy_(torch.randn((B, hkv, d), generator=gen).to(torch.bfloat16))
+        _say(f"torch-graph replay {it}")
+        tg.replay()
+        ref = [torch.empty_like(o) for o in outs]
+        step(pool_e, ref)
+        torch.cuda.synchronize()
+        for layer in range(NL):
+            assert torch.equal(outs[layer].view(torch.int16), ref[layer].view(torch.int16))
+        assert torch.equal(pool.view(torch.int16), pool_e.view(torch.int16))
