@@ -47,15 +47,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # reported as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_split_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "85f498656a1b99faf34b00bc595c4d1aac0e57984c30db640c254a01214aacb7",
+        "sources": {"decode.hip": "b6f914cb2fa3964c3b947892fc60ec8e588ae5f5b8b0fc6353479246ecbc7483",
                     "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
-        "bytes": 662501464,
+        "bytes": 660873376,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
-        "sources": {"extend.hip": "d705a03e97f4a81edfb03b7e2ac66a9a9fe75379c267c8aa7eff29aee7cac375",
+        "sources": {"extend.hip": "90f01e7c86aacad1887710ae444a49137dcf66ca674b6597038a1606559468ca",
                     "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
-        "bytes": 245847608,
+        "bytes": 239901568,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
 }
@@ -277,6 +277,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle work")
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the small decode-graph comparison (keeps profiles to the step's kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -367,8 +369,10 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    log("decode graph vs eager calls (small batch)")
-    graph_stats = graph_vs_eager(msgl, dev)
+    graph_stats = None
+    if not args.no_graph:
+        log("decode graph vs eager calls (small batch)")
+        graph_stats = graph_vs_eager(msgl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
