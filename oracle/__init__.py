@@ -13,3 +13,4 @@ from .paged_kv import (  # noqa: F401
     store_kv,
     token_slots,
 )
+from .rope import f64_to_bf16_bits, rope, rope_f64, rope_store_kv, rope_table  # noqa: F401
