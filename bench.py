@@ -202,6 +202,35 @@ def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
     }
 
 
+def rope_store_stats(msgl, p, dev, iters=20):
+    """The fused rotary embedding + store_kv over one extend phase's new
+    rows (positions prefix + i), as HBM throughput: algorithmic bytes are q
+    read and written, k and v read, K and V written, the table rows read
+    (one per token), out_loc and positions."""
+    wl, ph = p.wl, p.ph
+    pos = np.concatenate([np.arange(int(ph.prefix_lens[r]), int(ph.prefix_lens[r] + ph.extend_lens[r]))
+                          for r in range(ph.batch)]).astype(np.int32)
+    table = msgl.rope_cos_sin_table(int(pos.max()) + 1, wl.head_dim, 10000.0, device=dev)
+    posd = i32(pos, dev)
+    q = p.q.clone()
+    T, hq, d, hkv = q.shape[0], wl.num_qo_heads, wl.head_dim, wl.num_kv_heads
+    nbytes = T * (2 * hq * d * 2 + 2 * 2 * hkv * d * 2 + d * 4 + 8)
+    for _ in range(3):
+        msgl.rope_store_kv(p.pool, wl.layer, q, p.k, p.v, p.loc, posd, table)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        msgl.rope_store_kv(p.pool, wl.layer, q, p.k, p.v, p.loc, posd, table)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"rows": T, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
+            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def graph_vs_eager(msgl, dev, iters=300):
     """A small decode step -- store_kv of 8 new rows, then decode of 8
     requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
@@ -369,6 +398,8 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
+    log("fused rotary embedding + store_kv (extend rows)")
+    rope_stats = rope_store_stats(msgl, pe, dev)
     graph_stats = None
     if not args.no_graph:
         log("decode graph vs eager calls (small batch)")
@@ -441,6 +472,7 @@ def main():
         },
         "extend_tflops": round(ext_tflops, 2),
         "decode_graph": graph_stats,
+        "rope_store_kv": rope_stats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -172,6 +172,46 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
                               void* stream);
 
 /*
+ * rope_store_kv: rotary position embedding of this step's new rows, fused
+ * with store_kv ("Code Notes: mini-sglang", section "Layers", get_rope --
+ * rotary position embeddings; Engine Layer table, BaseKVCachePool row for
+ * the store).  For t < num_tokens, with p = positions[t]:
+ *   q[t, h, :] <- rope(q[t, h, :], p) in place, for every q head h;
+ *   K[layer] slot out_loc[t] <- rope(k[t], p), V[layer] slot <- v[t]
+ *   (rows with out_loc[t] < 0 store nothing; q is still rotated).
+ * rope pairs channel i < d/2 with channel i + d/2 and turns the pair by the
+ * angle whose cosine and sine are cos_sin_table[p*head_dim + i] and
+ * cos_sin_table[p*head_dim + head_dim/2 + i]:
+ *   y_i = x_i cos - x_{i+d/2} sin,  y_{i+d/2} = x_{i+d/2} cos + x_i sin.
+ * Each output is the exact value rounded once to bf16 (fp64 arithmetic).
+ *   q            : (num_tokens, num_qo_heads, head_dim) bf16, rows
+ *                  q_row_stride elements apart; may be NULL when
+ *                  num_qo_heads == 0.
+ *   k, v         : (num_tokens, num_kv_heads, head_dim), as for store_kv.
+ *   positions    : (num_tokens,) int32 in [0, max_position) (values outside
+ *                  are the caller's contract; they are clamped).
+ *   cos_sin_table: (max_position, head_dim) fp32, e.g. from
+ *                  msgl_rope_cos_sin_table.
+ * head_dim 64 or 128; q/k/v/pool 16-byte aligned with row strides a
+ * multiple of 8 elements; q rows must not overlap k or v rows.
+ */
+msgl_status msgl_rope_store_kv(const msgl_kv_pool* pool, int32_t layer, void* q,
+                               int64_t q_row_stride, int32_t num_qo_heads, const void* k,
+                               int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                               const int32_t* out_loc, const int32_t* positions,
+                               int32_t num_tokens, const float* cos_sin_table,
+                               int32_t max_position, void* stream);
+
+/*
+ * rope_cos_sin_table: fill table (max_position, head_dim) fp32 with
+ * cos(p * base^(-2i/d)) in columns i < d/2 and the sines in columns
+ * d/2 + i -- the angles, cosines and sines computed in fp64 and rounded
+ * once to fp32.  head_dim even and > 0, max_position > 0, base > 0.
+ */
+msgl_status msgl_rope_cos_sin_table(float* table, int32_t max_position, int32_t head_dim,
+                                    double base, void* stream);
+
+/*
  * Decode graphs: store_kv of one new row per request followed by
  * paged_decode, captured once into a HIP graph for a fixed (padded) batch
  * size and replayed with one launch ("Code Notes: mini-sglang", Engine

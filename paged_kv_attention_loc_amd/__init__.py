@@ -38,6 +38,10 @@ __all__ = [
     "paged_extend",
     "debug_gather_kv",
     "DecodeGraph",
+    "msgl_rope_store_kv",
+    "msgl_rope_cos_sin_table",
+    "rope_store_kv",
+    "rope_cos_sin_table",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +99,10 @@ def load_library():
                                       F32, P]
     lib.msgl_debug_gather_kv.restype = I32
     lib.msgl_debug_gather_kv.argtypes = [PP, I32, P, I32, I32, I32, P, P, P]
+    lib.msgl_rope_store_kv.restype = I32
+    lib.msgl_rope_store_kv.argtypes = [PP, I32, P, I64, I32, P, I64, P, I64, P, P, I32, P, I32, P]
+    lib.msgl_rope_cos_sin_table.restype = I32
+    lib.msgl_rope_cos_sin_table.argtypes = [P, I32, I32, ctypes.c_double, P]
     lib.msgl_decode_graph_create.restype = I32
     lib.msgl_decode_graph_create.argtypes = [PP, I32, P, I64, P, I64, P, P, I64, P, P, I32, P, P, I32,
                                              I32, I32, F32, P, SZ, ctypes.POINTER(P)]
@@ -237,6 +245,45 @@ def msgl_debug_gather_kv(pool: torch.Tensor, layer: int, page_table: torch.Tenso
     return k, v
 
 
+def msgl_rope_cos_sin_table(max_position: int, head_dim: int, base: float = 10000.0,
+                            device="cuda") -> torch.Tensor:
+    """(max_position, head_dim) fp32: cos of p * base^(-2i/d) in columns
+    i < d/2, the sines after them (computed by the library kernel)."""
+    t = torch.empty((max_position, head_dim), dtype=torch.float32, device=device)
+    st = load_library().msgl_rope_cos_sin_table(t.data_ptr(), int(max_position), int(head_dim),
+                                                float(base), _stream(t))
+    _check(st, "msgl_rope_cos_sin_table")
+    return t
+
+
+def msgl_rope_store_kv(pool: torch.Tensor, layer: int, q: Optional[torch.Tensor], k: torch.Tensor,
+                       v: torch.Tensor, out_loc: torch.Tensor, positions: torch.Tensor,
+                       cos_sin_table: torch.Tensor) -> None:
+    """Rotate q in place and store rotated k and v at out_loc (one launch)."""
+    ps = _pool_struct(pool)
+    T = int(out_loc.numel())
+    ks = _rows(k, "k", ps.num_kv_heads, ps.head_dim)
+    vs = _rows(v, "v", ps.num_kv_heads, ps.head_dim)
+    if k.shape[0] != T or v.shape[0] != T or positions.numel() != T:
+        raise ValueError("k, v, out_loc and positions must have the same number of rows")
+    if q is not None:
+        hq = int(q.shape[1])
+        qs = _rows(q, "q", hq, ps.head_dim)
+        if q.shape[0] != T:
+            raise ValueError("q must have one row per token")
+        qp = q.data_ptr()
+    else:
+        hq, qs, qp = 0, 0, None
+    if (cos_sin_table.dtype != torch.float32 or cos_sin_table.dim() != 2 or not cos_sin_table.is_cuda
+            or cos_sin_table.shape[1] != ps.head_dim or not cos_sin_table.is_contiguous()):
+        raise ValueError("cos_sin_table must be a contiguous (max_position, head_dim) fp32 CUDA tensor")
+    st = load_library().msgl_rope_store_kv(
+        ctypes.byref(ps), layer, qp, qs, hq, k.data_ptr(), ks, v.data_ptr(), vs,
+        _i32(out_loc, "out_loc"), _i32(positions, "positions"), T, cos_sin_table.data_ptr(),
+        int(cos_sin_table.shape[0]), _stream(pool))
+    _check(st, "msgl_rope_store_kv")
+
+
 class DecodeGraph:
     """store_kv of one new K/V row per request + paged decode, captured once
     for a fixed padded batch and replayed with a single graph launch
@@ -332,6 +379,8 @@ class DecodeGraph:
 
 # short names
 store_kv = msgl_store_kv
+rope_store_kv = msgl_rope_store_kv
+rope_cos_sin_table = msgl_rope_cos_sin_table
 paged_decode = msgl_paged_decode
 paged_decode_workspace_size = msgl_paged_decode_workspace_size
 paged_extend = msgl_paged_extend

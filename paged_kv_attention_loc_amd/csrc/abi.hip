@@ -409,6 +409,78 @@ msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,
   return hip_status(launch_gather(p, static_cast<hipStream_t>(stream)));
 }
 
+msgl_status msgl_rope_store_kv(const msgl_kv_pool* pool, int32_t layer, void* q,
+                               int64_t q_row_stride, int32_t num_qo_heads, const void* k,
+                               int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                               const int32_t* out_loc, const int32_t* positions,
+                               int32_t num_tokens, const float* cos_sin_table,
+                               int32_t max_position, void* stream) {
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (num_tokens < 0 || num_qo_heads < 0 || max_position < 1) return MSGL_ERR_SHAPE;
+  if (num_tokens == 0) return MSGL_OK;
+  if (!k || !v || !out_loc || !positions || !cos_sin_table || (num_qo_heads > 0 && !q))
+    return MSGL_ERR_NULL;
+  const int32_t d = pool->head_dim;
+  if (d != 64 && d != 128) return MSGL_ERR_UNSUPPORTED;
+  const int64_t row = static_cast<int64_t>(pool->num_kv_heads) * d;
+  if (k_row_stride < row || v_row_stride < row || (k_row_stride % 8) != 0 ||
+      (v_row_stride % 8) != 0 || !aligned16(k) || !aligned16(v) || !aligned16(pool->data) ||
+      !aligned16(cos_sin_table))
+    return MSGL_ERR_SHAPE;
+  if (num_qo_heads > 0 && (q_row_stride < static_cast<int64_t>(num_qo_heads) * d ||
+                           (q_row_stride % 8) != 0 || !aligned16(q)))
+    return MSGL_ERR_SHAPE;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    std::vector<int32_t> loc, pos;
+    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens)) ||
+        !copy_to_host(pos, positions, static_cast<size_t>(num_tokens)))
+      return MSGL_ERR_HIP;
+    std::vector<uint8_t> seen(static_cast<size_t>(num_slots(pool)), 0);
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (pos[i] < 0 || pos[i] >= max_position || loc[i] >= num_slots(pool)) return MSGL_ERR_RANGE;
+      if (loc[i] >= 0) {
+        if (seen[loc[i]]) return MSGL_ERR_RANGE;
+        seen[loc[i]] = 1;
+      }
+    }
+  }
+  RopeParams p;
+  p.q = static_cast<uint16_t*>(q);
+  p.q_stride = q_row_stride;
+  p.k = static_cast<const uint16_t*>(k);
+  p.k_stride = k_row_stride;
+  p.v = static_cast<const uint16_t*>(v);
+  p.v_stride = v_row_stride;
+  p.out_loc = out_loc;
+  p.positions = positions;
+  p.table = cos_sin_table;
+  p.k_cache = const_cast<uint16_t*>(k_half(pool, layer));
+  p.v_cache = const_cast<uint16_t*>(v_half(pool, layer));
+  p.num_qo_heads = num_qo_heads;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = d;
+  p.max_position = max_position;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  const int64_t per_tok = static_cast<int64_t>(num_qo_heads + pool->num_kv_heads) * (d / 16) +
+                          static_cast<int64_t>(pool->num_kv_heads) * (d / 8);
+  p.num_items = per_tok * num_tokens;
+  return hip_status(launch_rope_store_kv(p, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_rope_cos_sin_table(float* table, int32_t max_position, int32_t head_dim,
+                                    double base, void* stream) {
+  if (max_position < 1 || head_dim < 2 || (head_dim % 2) != 0 || !(base > 0.0))
+    return MSGL_ERR_SHAPE;
+  if (!table) return MSGL_ERR_NULL;
+  const msgl_status st = check_device();
+  if (st != MSGL_OK) return st;
+  return hip_status(launch_rope_table(table, max_position, head_dim, base,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, const void* k,
                                      int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                      const int32_t* out_loc, const void* q, int64_t q_row_stride,

@@ -195,6 +195,26 @@ struct ExtendParams {
   float scale_log2;
 };
 
+struct RopeParams {
+  uint16_t* q;          // rotated in place
+  int64_t q_stride;     // elements between rows
+  const uint16_t* k;
+  int64_t k_stride;
+  const uint16_t* v;
+  int64_t v_stride;
+  const int32_t* out_loc;
+  const int32_t* positions;
+  const float* table;   // (max_position, head_dim): cos then sin
+  uint16_t* k_cache;    // K half of the layer, (slots, Hkv, d)
+  uint16_t* v_cache;
+  int64_t num_items;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_position;
+  int32_t num_slots;
+};
+
 // Launchers (defined next to their kernels); return the HIP status.
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
@@ -203,5 +223,8 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStre
 // caller sizes p.num_mtiles for it.
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,
                          hipStream_t stream);
+hipError_t launch_rope_store_kv(const RopeParams& p, hipStream_t stream);
+hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double base,
+                             hipStream_t stream);
 
 }  // namespace msgl

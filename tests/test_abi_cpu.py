@@ -169,3 +169,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
             msgl.load_library()
     finally:
         msgl._lib = saved
+
+
+def test_rope_calls_reject_bad_arguments_without_launch():
+    lib = _lib()
+    P = ctypes.c_void_p
+    f = lib.msgl_rope_store_kv
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int64, P,
+                  ctypes.c_int64, P, P, ctypes.c_int32, P, ctypes.c_int32, P]
+    assert f(None, 0, None, 0, 0, None, 0, None, 0, None, None, 1, None, 1, None) == 1  # NULL pool
+    fake = ctypes.c_void_p(0x1000)
+    pool = msgl._Pool(fake.value, 1, 4, 16, 2, 128)
+    # max_position 0
+    assert f(ctypes.byref(pool), 0, None, 0, 0, fake, 256, fake, 256, fake, fake, 3, fake, 0,
+             None) == 2
+    # head_dim 96 is not supported
+    pool96 = msgl._Pool(fake.value, 1, 4, 16, 2, 96)
+    assert f(ctypes.byref(pool96), 0, None, 0, 0, fake, 192, fake, 192, fake, fake, 3, fake, 8,
+             None) == 3
+    # a q with too short a row
+    assert f(ctypes.byref(pool), 0, fake, 64, 4, fake, 256, fake, 256, fake, fake, 3, fake, 8,
+             None) == 2
+    g = lib.msgl_rope_cos_sin_table
+    g.restype = ctypes.c_int32
+    g.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P]
+    assert g(fake, 16, 63, 10000.0, None) == 2  # odd head_dim
+    assert g(fake, 0, 64, 10000.0, None) == 2
+    assert g(fake, 16, 64, -1.0, None) == 2
+    assert g(None, 16, 64, 10000.0, None) == 1
