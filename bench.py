@@ -48,13 +48,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 MEASURED_TRAFFIC = {
     "decode": {  # decode_split_kernel + decode_merge_kernel
         "sources": {"decode.hip": "b6f914cb2fa3964c3b947892fc60ec8e588ae5f5b8b0fc6353479246ecbc7483",
-                    "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
+                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758"},
         "bytes": 660873376,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
         "sources": {"extend.hip": "90f01e7c86aacad1887710ae444a49137dcf66ca674b6597038a1606559468ca",
-                    "common.h": "7651d4fbddf1ff3d866a2d5783d9fc95b30c46b04cd75f2af7d3bcc133a10796"},
+                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758"},
         "bytes": 239901568,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
