@@ -42,20 +42,22 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch from two rocprofv3 --pmc runs of this benchmark
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
 # for a plain 512 MiB device copy (x2 for FETCH_SIZE, x1 for WRITE_SIZE),
-# taken on the kernel sources with these SHA-256 digests.  When a source
-# has changed since, the figure no longer describes the kernel and is
-# reported as null.
+# taken on the kernel sources (and abi.hip, which sets the launch
+# configuration) with these SHA-256 digests.  When a source has changed
+# since, the figure no longer describes the kernel and is reported as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_split_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "b6f914cb2fa3964c3b947892fc60ec8e588ae5f5b8b0fc6353479246ecbc7483",
-                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758"},
-        "bytes": 660873376,
+        "sources": {"decode.hip": "64ab301b1f7358b2dca5724b9878aadeb5b51c64453e04840e908b37dad1468c",
+                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758",
+                    "abi.hip": "8148f30c4df268ead72718e0d4cad2d62d7d99df50a7f1f341d65c82cf9cf4c9"},
+        "bytes": 653295840,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
         "sources": {"extend.hip": "90f01e7c86aacad1887710ae444a49137dcf66ca674b6597038a1606559468ca",
-                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758"},
-        "bytes": 239901568,
+                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758",
+                    "abi.hip": "8148f30c4df268ead72718e0d4cad2d62d7d99df50a7f1f341d65c82cf9cf4c9"},
+        "bytes": 240123648,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
 }

@@ -94,11 +94,12 @@ int extend_waves() {
   return (v && std::atoi(v) == 4) ? 4 : 8;
 }
 
-// Tokens per decode split (a multiple of 64): 256 by default, measured best
-// on the Llama-3-8B and Qwen3-30B-A3B geometry batches; MSGL_DECODE_SPLIT
-// overrides it.
+// Tokens per decode split (a multiple of 64): 384 by default.  Measured
+// over 128-512 with nontemporal K/V loads, 256-384 tie on the Llama-3-8B
+// geometry batch and 384 is ~3% faster on the Qwen3-30B-A3B one (long,
+// lognormal lengths: fewer partials).  MSGL_DECODE_SPLIT overrides it.
 int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_seq_len) {
-  int64_t c = 256;
+  int64_t c = 384;
   const char* v = std::getenv("MSGL_DECODE_SPLIT");
   if (v && v[0]) {
     const long e = std::strtol(v, nullptr, 10);

@@ -11,7 +11,7 @@
 // One wave64 workgroup handles (request, kv head, chunk of `chunk` tokens)
 // in tiles of 32 tokens.  A wave needs about 9-11 KiB of LDS and few
 // registers, so a CU holds 16 of them and their loads overlap each other's
-// arithmetic; chunks are short (256 tokens by default) so that many
+// arithmetic; chunks are short (384 tokens by default) so that many
 // independent waves are in flight while the split partials stay a few
 // percent of the KV bytes.
 //   * the K/V loads carry the nontemporal hint: every byte is read once;

@@ -64,9 +64,9 @@ def _pool(**kw):
 def test_workspace_size_is_host_arithmetic():
     lib = _lib()
     f = lib.msgl_paged_decode_workspace_size
-    assert f(64, 32, 8, 128, 256) == 0  # one split: no partials
+    assert f(64, 32, 8, 128, 384) == 0  # one split: no partials
     n = f(64, 32, 8, 128, 4096)
-    chunks = 4096 // 256
+    chunks = -(-4096 // 384)
     units = 64 * chunks * (32 + 1)  # one padding unit per (request, chunk)
     assert n == ((units * 128 * 4 + 255) // 256) * 256 + units * 8
     assert f(-1, 32, 8, 128, 4096) == 0
