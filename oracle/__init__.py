@@ -13,4 +13,5 @@ from .paged_kv import (  # noqa: F401
     store_kv,
     token_slots,
 )
+from .alloc import alloc_pages  # noqa: F401
 from .rope import f64_to_bf16_bits, rope, rope_f64, rope_store_kv, rope_table  # noqa: F401
