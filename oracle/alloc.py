@@ -19,8 +19,10 @@ mapping).  The reading taken for one scheduling step:
   * out_loc lists the slot of every new token, requests in order, token
     P_r + i of request r at page_table[row, (P_r + i) // page_size] *
     page_size + (P_r + i) % page_size;
-  * if the step needs more pages than are free, nothing is taken or
-    written and the step is reported as failed.
+  * a step that cannot be done -- more pages needed than are free, a row
+    that would need more entries than the page table has, a negative
+    length or a row index outside the table -- takes and writes nothing
+    and is reported as failed.
 """
 
 from __future__ import annotations
@@ -38,12 +40,18 @@ def alloc_pages(free_pages: np.ndarray, num_free: int, page_table: np.ndarray,
     P = np.asarray(prefix_lens, dtype=np.int64)
     E = np.asarray(extend_lens, dtype=np.int64)
     ps = int(page_size)
+    rows = np.asarray(table_idx, dtype=np.int64)
+    out_loc = np.zeros(max(int(E.clip(min=0).sum()), 0), dtype=np.int32)
+    unchanged = (False, int(num_free), np.array(page_table, dtype=np.int32, copy=True), out_loc)
+    if np.any(P < 0) or np.any(E < 0) or np.any(rows < 0) or np.any(rows >= pt.shape[0]):
+        return unchanged
     have = (P + ps - 1) // ps
     need = (P + E + ps - 1) // ps - have
+    if np.any(have + need > pt.shape[1]):
+        return unchanged
     total = int(need.sum())
-    out_loc = np.zeros(int(E.sum()), dtype=np.int32)
     if total > num_free:
-        return False, int(num_free), np.array(page_table, dtype=np.int32, copy=True), out_loc
+        return unchanged
     k = 0
     t = 0
     for r in range(len(P)):

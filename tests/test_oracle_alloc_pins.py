@@ -78,8 +78,12 @@ def test_a2_random_step_invariants(seed, ps):
         t += int(E[r])
 
 
-def test_a3_not_enough_pages_changes_nothing():
+def test_a3_impossible_steps_change_nothing():
     free = np.array([5, 6], np.int32)
     pt = np.full((2, 8), -1, np.int32)
-    ok, nf, pt2, loc = oracle.alloc_pages(free, 2, pt, [0, 1], [0, 0], [9, 1], 4)
-    assert not ok and nf == 2 and np.array_equal(pt2, pt)
+    for rows, P, E in (([0, 1], [0, 0], [9, 1]),    # 4 pages needed, 2 free
+                       ([0, 1], [0, 0], [33, 0]),   # 9 entries > 8 in the row
+                       ([0, 1], [0, 0], [1, -1]),   # negative length
+                       ([0, 2], [0, 0], [1, 1])):   # row 2 outside the table
+        ok, nf, pt2, loc = oracle.alloc_pages(free, 2, pt, rows, P, E, 4)
+        assert not ok and nf == 2 and np.array_equal(pt2, pt)
