@@ -212,6 +212,36 @@ msgl_status msgl_rope_cos_sin_table(float* table, int32_t max_position, int32_t 
                                     double base, void* stream);
 
 /*
+ * alloc_pages: device-side page allocation for one scheduling step
+ * ("Code Notes: mini-sglang", Scheduler Layer table: CacheManager row --
+ * free_slots, the free positions handed out to new tokens; TableManager
+ * row -- one page_table row per request).  With P_r = prefix_lens[r]
+ * tokens already held (ceil(P_r/page_size) pages in row table_idx[r]) and
+ * E_r = extend_lens[r] new tokens:
+ *   - request r receives ceil((P_r+E_r)/page_size) - ceil(P_r/page_size)
+ *     pages, written to the next entries of its row;
+ *   - pages are taken from the tail of the free list, requests in order:
+ *     the k-th page taken is free_pages[*num_free - 1 - k];
+ *   - out_loc (sum E_r entries, requests in order) receives the slot of
+ *     every new token, position P_r + i of request r through its row;
+ *   - *num_free drops by the number of pages taken.
+ * All arrays and *num_free are on the device; nothing is read back to the
+ * host, so a step can be enqueued (or captured) with no synchronisation.
+ * *status (device) is set to 0 when the step is done; otherwise nothing is
+ * written and it says why: 1 not enough free pages, 2 a row would exceed
+ * page_table_stride entries, 3 a negative length or a table_idx outside
+ * [0, page_table_rows), 4 out_loc_capacity below sum E_r.  The pages each
+ * request already holds must be valid ids, rows must be distinct, and the
+ * free list must hold *num_free valid, unused page ids (caller's contract).
+ */
+msgl_status msgl_alloc_pages(const int32_t* free_pages, int32_t* num_free, int32_t* page_table,
+                             int32_t page_table_stride, int32_t page_table_rows,
+                             const int32_t* table_idx, const int32_t* prefix_lens,
+                             const int32_t* extend_lens, int32_t batch, int32_t page_size,
+                             int32_t* out_loc, int64_t out_loc_capacity, int32_t* status,
+                             void* stream);
+
+/*
  * Decode graphs: store_kv of one new row per request followed by
  * paged_decode, captured once into a HIP graph for a fixed (padded) batch
  * size and replayed with one launch ("Code Notes: mini-sglang", Engine

@@ -42,6 +42,8 @@ __all__ = [
     "msgl_rope_cos_sin_table",
     "rope_store_kv",
     "rope_cos_sin_table",
+    "msgl_alloc_pages",
+    "alloc_pages",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +105,8 @@ def load_library():
     lib.msgl_rope_store_kv.argtypes = [PP, I32, P, I64, I32, P, I64, P, I64, P, P, I32, P, I32, P]
     lib.msgl_rope_cos_sin_table.restype = I32
     lib.msgl_rope_cos_sin_table.argtypes = [P, I32, I32, ctypes.c_double, P]
+    lib.msgl_alloc_pages.restype = I32
+    lib.msgl_alloc_pages.argtypes = [P, P, P, I32, I32, P, P, P, I32, I32, P, I64, P, P]
     lib.msgl_decode_graph_create.restype = I32
     lib.msgl_decode_graph_create.argtypes = [PP, I32, P, I64, P, I64, P, P, I64, P, P, I32, P, P, I32,
                                              I32, I32, F32, P, SZ, ctypes.POINTER(P)]
@@ -245,6 +249,27 @@ def msgl_debug_gather_kv(pool: torch.Tensor, layer: int, page_table: torch.Tenso
     return k, v
 
 
+def msgl_alloc_pages(free_pages: torch.Tensor, num_free: torch.Tensor, page_table: torch.Tensor,
+                     table_idx: torch.Tensor, prefix_lens: torch.Tensor, extend_lens: torch.Tensor,
+                     page_size: int, out_loc: torch.Tensor, status: torch.Tensor) -> None:
+    """One scheduling step's page allocation on the device (see msgl.h):
+    new pages from the tail of free_pages[:num_free] into the page_table
+    rows, out_loc filled, num_free and status (both 1-element int32 device
+    tensors) updated.  Nothing is read back to the host."""
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D (rows, entries)")
+    B = int(table_idx.numel())
+    for name, t in (("num_free", num_free), ("status", status)):
+        if t.numel() < 1:
+            raise ValueError(f"{name} must hold one int32")
+    st = load_library().msgl_alloc_pages(
+        _i32(free_pages, "free_pages"), _i32(num_free, "num_free"), _i32(page_table, "page_table"),
+        int(page_table.shape[1]), int(page_table.shape[0]), _i32(table_idx, "table_idx"),
+        _i32(prefix_lens, "prefix_lens"), _i32(extend_lens, "extend_lens"), B, int(page_size),
+        _i32(out_loc, "out_loc"), int(out_loc.numel()), _i32(status, "status"), _stream(page_table))
+    _check(st, "msgl_alloc_pages")
+
+
 def msgl_rope_cos_sin_table(max_position: int, head_dim: int, base: float = 10000.0,
                             device="cuda") -> torch.Tensor:
     """(max_position, head_dim) fp32: cos of p * base^(-2i/d) in columns
@@ -381,6 +406,7 @@ class DecodeGraph:
 store_kv = msgl_store_kv
 rope_store_kv = msgl_rope_store_kv
 rope_cos_sin_table = msgl_rope_cos_sin_table
+alloc_pages = msgl_alloc_pages
 paged_decode = msgl_paged_decode
 paged_decode_workspace_size = msgl_paged_decode_workspace_size
 paged_extend = msgl_paged_extend

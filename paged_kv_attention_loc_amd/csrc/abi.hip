@@ -482,6 +482,38 @@ msgl_status msgl_rope_cos_sin_table(float* table, int32_t max_position, int32_t 
                                       static_cast<hipStream_t>(stream)));
 }
 
+msgl_status msgl_alloc_pages(const int32_t* free_pages, int32_t* num_free, int32_t* page_table,
+                             int32_t page_table_stride, int32_t page_table_rows,
+                             const int32_t* table_idx, const int32_t* prefix_lens,
+                             const int32_t* extend_lens, int32_t batch, int32_t page_size,
+                             int32_t* out_loc, int64_t out_loc_capacity, int32_t* status,
+                             void* stream) {
+  if (batch < 0 || page_size < 1 || page_table_stride < 1 || page_table_rows < 1 ||
+      out_loc_capacity < 0)
+    return MSGL_ERR_SHAPE;
+  if (!num_free || !page_table || !status || (batch > 0 && (!table_idx || !prefix_lens ||
+                                                            !extend_lens)) ||
+      (out_loc_capacity > 0 && !out_loc) || !free_pages)
+    return MSGL_ERR_NULL;
+  const msgl_status st = check_device();
+  if (st != MSGL_OK) return st;
+  AllocParams p;
+  p.free_pages = free_pages;
+  p.num_free = num_free;
+  p.page_table = page_table;
+  p.pt_stride = page_table_stride;
+  p.pt_rows = page_table_rows;
+  p.table_idx = table_idx;
+  p.prefix_lens = prefix_lens;
+  p.extend_lens = extend_lens;
+  p.batch = batch;
+  p.page_size = page_size;
+  p.out_loc = out_loc;
+  p.out_loc_capacity = out_loc_capacity;
+  p.status = status;
+  return hip_status(launch_alloc_pages(p, static_cast<hipStream_t>(stream)));
+}
+
 msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, const void* k,
                                      int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                      const int32_t* out_loc, const void* q, int64_t q_row_stride,

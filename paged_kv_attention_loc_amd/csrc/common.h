@@ -215,6 +215,22 @@ struct RopeParams {
   int32_t num_slots;
 };
 
+struct AllocParams {
+  const int32_t* free_pages;
+  int32_t* num_free;       // device count of free pages, updated in place
+  int32_t* page_table;
+  int64_t pt_stride;
+  int32_t pt_rows;
+  const int32_t* table_idx;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  int32_t batch;
+  int32_t page_size;
+  int32_t* out_loc;
+  int64_t out_loc_capacity;
+  int32_t* status;         // device: 0 done, else why nothing was done
+};
+
 // Launchers (defined next to their kernels); return the HIP status.
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
@@ -224,6 +240,7 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStre
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,
                          hipStream_t stream);
 hipError_t launch_rope_store_kv(const RopeParams& p, hipStream_t stream);
+hipError_t launch_alloc_pages(const AllocParams& p, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double base,
                              hipStream_t stream);
 

@@ -198,3 +198,26 @@ def test_rope_calls_reject_bad_arguments_without_launch():
     assert g(fake, 0, 64, 10000.0, None) == 2
     assert g(fake, 16, 64, -1.0, None) == 2
     assert g(None, 16, 64, 10000.0, None) == 1
+
+
+def test_alloc_pages_rejects_bad_arguments_without_launch():
+    lib = _lib()
+    P = ctypes.c_void_p
+    f = lib.msgl_alloc_pages
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_int32, ctypes.c_int32,
+                  P, ctypes.c_int64, P, P]
+    fake = ctypes.c_void_p(0x1000)
+    ok_args = [fake, fake, fake, 8, 4, fake, fake, fake, 2, 16, fake, 10, fake, None]
+    bad = list(ok_args)
+    bad[9] = 0  # page_size
+    assert f(*bad) == 2
+    bad = list(ok_args)
+    bad[8] = -1  # batch
+    assert f(*bad) == 2
+    bad = list(ok_args)
+    bad[1] = None  # num_free
+    assert f(*bad) == 1
+    bad = list(ok_args)
+    bad[10] = None  # out_loc with a capacity
+    assert f(*bad) == 1
