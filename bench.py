@@ -233,6 +233,32 @@ def rope_store_stats(msgl, p, dev, iters=20):
             "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def alloc_stats(msgl, p, dev, iters=50):
+    """msgl_alloc_pages for one phase's new tokens (a copy of its page table,
+    the pool's unused pages as the free list); the free count is reset
+    before each timed launch."""
+    wl, ph = p.wl, p.ph
+    pt = p.pt.clone()
+    used = np.unique(wl.page_table[wl.page_table >= 0])
+    free = np.setdiff1d(np.arange(wl.num_pages, dtype=np.int32), used).astype(np.int32)
+    d_free = i32(free, dev)
+    d_nfree = torch.zeros(1, dtype=torch.int32, device=dev)
+    d_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out_loc = torch.empty(ph.num_tokens, dtype=torch.int32, device=dev)
+    ts = []
+    for i in range(iters + 3):
+        d_nfree.fill_(len(free))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        msgl.alloc_pages(d_free, d_nfree, pt, p.ti, p.pl, p.el, wl.page_size, out_loc, d_status)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(a.elapsed_time(b) * 1e3)
+    assert int(d_status.item()) == 0
+    return {"requests": ph.batch, "new_tokens": ph.num_tokens, "avg_launch_us": round(float(np.mean(ts)), 2)}
+
+
 def graph_vs_eager(msgl, dev, iters=300):
     """A small decode step -- store_kv of 8 new rows, then decode of 8
     requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
@@ -400,6 +426,8 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
+    log("device-side page allocation")
+    alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
     log("fused rotary embedding + store_kv (extend rows)")
     rope_stats = rope_store_stats(msgl, pe, dev)
     graph_stats = None
@@ -475,6 +503,7 @@ def main():
         "extend_tflops": round(ext_tflops, 2),
         "decode_graph": graph_stats,
         "rope_store_kv": rope_stats,
+        "alloc_pages": alloc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

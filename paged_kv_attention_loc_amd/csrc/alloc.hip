@@ -21,10 +21,10 @@
 //
 // One workgroup of 1024 threads: a first pass checks every request and
 // sums the demand; a second walks the requests in chunks of 1024, where
-// block-wide exclusive scans give each request its first page and first
-// token, the request's thread writes its pages, and all threads then fill
-// the chunk's out_loc entries (a binary search over the token offsets
-// finds each token's request).
+// block-wide exclusive scans (wave shuffles, then the wave totals) give
+// each request its first page and first token, the request's thread writes
+// its pages, and all threads then fill the chunk's out_loc entries (a
+// binary search over the token offsets finds each token's request).
 #include "common.h"
 
 namespace msgl {
@@ -33,28 +33,43 @@ namespace {
 
 constexpr int kAllocThreads = 1024;
 
-// exclusive prefix sum of v over the block (Hillis-Steele in LDS); returns
-// this thread's exclusive sum and leaves the block total in *total
-__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* buf, int64_t* total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kAllocThreads; off <<= 1) {
-    const int64_t add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// exclusive prefix sum of v over the block; returns this thread's
+// exclusive sum and leaves the block total in *total.  Each wave scans its
+// 64 values with shuffles, wave 0 scans the 16 wave totals, and every
+// thread adds the totals of the waves before its own: three barriers.
+// `wave_tot` holds 32 values (the totals, then their inclusive sums).
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* wave_tot, int64_t* total) {
+  constexpr int kWaves = kAllocThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int64_t incl = buf[t];
-  *total = buf[kAllocThreads - 1];
+  if (lane == 63) wave_tot[w] = x;
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+    int64_t tw = lane < kWaves ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int64_t y = __shfl_up(tw, off, 64);
+      if (lane >= off) tw += y;
+    }
+    if (lane < kWaves) wave_tot[kWaves + lane] = tw;
+  }
+  __syncthreads();
+  const int64_t before = w > 0 ? wave_tot[kWaves + w - 1] : 0;
+  *total = wave_tot[2 * kWaves - 1];
+  __syncthreads();  // wave_tot is reused by the next scan
+  return before + x - v;
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kAllocThreads) void alloc_pages_kernel(AllocParams p) {
-  __shared__ int64_t scan_buf[kAllocThreads];
+  __shared__ int64_t scan_buf[2 * (kAllocThreads / 64)];
   __shared__ int64_t tok_first[kAllocThreads];  // exclusive token offsets of the chunk
   __shared__ int32_t req_row[kAllocThreads];
   __shared__ int32_t req_pos0[kAllocThreads];
