@@ -286,6 +286,35 @@ msgl_status msgl_decode_graph_launch(const msgl_decode_graph* graph, void* strea
 msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph);
 
 /*
+ * paged_mixed: one call for a batch that mixes decode rows and
+ * prefill/extend rows, as a scheduler that runs chunked prefill beside
+ * decoding builds it ("Code Notes: mini-sglang", Engine Layer table,
+ * BaseAttnBackend row -- HybridBackend keeps a prefill and a decode
+ * backend; Scheduler Layer table, PrefillManager row -- chunked prefill).
+ * Arguments as for paged_extend, plus the decode workspace:
+ * msgl_paged_decode_workspace_size(batch, num_qo_heads, num_kv_heads,
+ * head_dim, max_seq_len) bytes.  Rows are dispatched on the device by
+ * extend_lens, so the host never needs the lengths:
+ *   - a row with extend_lens[r] == 1 is a decode row: split-KV decode and
+ *     merge, with q / out row cu_extend_lens[r] and length
+ *     prefix_lens[r] + 1;
+ *   - every other row goes through the extend kernel (rows with
+ *     extend_lens[r] == 0 produce nothing).
+ * The result equals paged_extend on the same batch within the attention
+ * tolerance; the decode rows equal paged_decode on those rows exactly.
+ * Three launches on `stream` (split decode, merge, extend); calls sharing a
+ * workspace must not overlap.
+ */
+msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                             int64_t q_row_stride, void* out, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* table_idx,
+                             const int32_t* prefix_lens, const int32_t* extend_lens,
+                             const int32_t* cu_extend_lens, int32_t batch,
+                             int32_t total_extend_tokens, int32_t max_extend_len,
+                             int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * debug_gather_kv (for tests): copy tokens 0 .. len-1 of page_table row
  * `row` out of the pool in logical order -- the page-table address
  * translation the attention kernels use, exposed on its own.

@@ -44,6 +44,8 @@ __all__ = [
     "rope_cos_sin_table",
     "msgl_alloc_pages",
     "alloc_pages",
+    "msgl_paged_mixed",
+    "paged_mixed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +107,9 @@ def load_library():
     lib.msgl_rope_store_kv.argtypes = [PP, I32, P, I64, I32, P, I64, P, I64, P, P, I32, P, I32, P]
     lib.msgl_rope_cos_sin_table.restype = I32
     lib.msgl_rope_cos_sin_table.argtypes = [P, I32, I32, ctypes.c_double, P]
+    lib.msgl_paged_mixed.restype = I32
+    lib.msgl_paged_mixed.argtypes = [PP, I32, P, I64, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
+                                     F32, P, SZ, P]
     lib.msgl_alloc_pages.restype = I32
     lib.msgl_alloc_pages.argtypes = [P, P, P, I32, I32, P, P, P, I32, I32, P, I64, P, P]
     lib.msgl_decode_graph_create.restype = I32
@@ -233,6 +238,39 @@ def msgl_paged_extend(pool: torch.Tensor, layer: int, q: torch.Tensor, page_tabl
         _i32(extend_lens, "extend_lens"), _i32(cu_extend_lens, "cu_extend_lens"), B, T,
         int(max_extend_len), int(max_seq_len), hq, float(sm_scale), _stream(q))
     _check(st, "msgl_paged_extend")
+    return out
+
+
+def msgl_paged_mixed(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
+                     table_idx: torch.Tensor, prefix_lens: torch.Tensor, extend_lens: torch.Tensor,
+                     cu_extend_lens: torch.Tensor, max_extend_len: int, max_seq_len: int,
+                     sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A batch of decode rows (one new token) and extend rows in one call:
+    q (sum E, Hq, d) -> out, rows dispatched on the device by extend_lens."""
+    ps = _pool_struct(pool)
+    T, hq, d = q.shape
+    qs = _rows(q, "q", hq, d)
+    B = int(table_idx.numel())
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.bfloat16, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    need = msgl_paged_decode_workspace_size(B, hq, ps.num_kv_heads, d, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D (rows, entries)")
+    st = load_library().msgl_paged_mixed(
+        ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
+        int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(prefix_lens, "prefix_lens"),
+        _i32(extend_lens, "extend_lens"), _i32(cu_extend_lens, "cu_extend_lens"), B, T,
+        int(max_extend_len), int(max_seq_len), hq, float(sm_scale), ws_ptr, ws_bytes, _stream(q))
+    _check(st, "msgl_paged_mixed")
     return out
 
 
@@ -407,6 +445,7 @@ store_kv = msgl_store_kv
 rope_store_kv = msgl_rope_store_kv
 rope_cos_sin_table = msgl_rope_cos_sin_table
 alloc_pages = msgl_alloc_pages
+paged_mixed = msgl_paged_mixed
 paged_decode = msgl_paged_decode
 paged_decode_workspace_size = msgl_paged_decode_workspace_size
 paged_extend = msgl_paged_extend

@@ -130,6 +130,146 @@ msgl_status check_row_pages(const int32_t* page_table, int64_t stride, int32_t r
   return MSGL_OK;
 }
 
+// Kernel parameters of a decode over validated arguments (workspace NULL
+// when no request needs more than one split).
+DecodeParams decode_params(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                           int64_t q_row_stride, void* out, const int32_t* page_table,
+                           int32_t page_table_stride, const int32_t* table_idx,
+                           const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
+                           int32_t max_seq_len, float sm_scale, void* workspace) {
+  const int32_t d = pool->head_dim;
+  DecodeParams p;
+  p.k_cache = k_half(pool, layer);
+  p.v_cache = v_half(pool, layer);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_stride = q_row_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.page_table = page_table;
+  p.pt_stride = page_table_stride;
+  p.table_idx = table_idx;
+  p.seq_lens = seq_lens;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.group = num_qo_heads / pool->num_kv_heads;
+  p.page_size = pool->page_size;
+  p.chunk = decode_chunk(batch, pool->num_kv_heads, max_seq_len);
+  p.max_chunks = static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + p.chunk - 1) / p.chunk);
+  if (p.max_chunks < 1) p.max_chunks = 1;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
+  p.page_shift = page_shift_of(pool->page_size);
+  p.max_seq_len = max_seq_len;
+  p.scale_log2 = sm_scale * kLog2e;
+  p.mixed_prefix = nullptr;
+  p.mixed_extend = nullptr;
+  p.mixed_cu = nullptr;
+  if (workspace) {
+    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * (num_qo_heads + 1);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_ml = reinterpret_cast<float*>(ws + ((units * d * 4 + 255) / 256) * 256);
+  } else {
+    p.ws_o = nullptr;
+    p.ws_ml = nullptr;
+  }
+  return p;
+}
+
+// Kernel parameters of an extend over validated arguments.
+ExtendParams extend_params(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                           int64_t q_row_stride, void* out, const int32_t* page_table,
+                           int32_t page_table_stride, const int32_t* table_idx,
+                           const int32_t* prefix_lens, const int32_t* extend_lens,
+                           const int32_t* cu_extend_lens, int32_t num_qo_heads, int32_t mtiles,
+                           int32_t max_extend_len, int32_t max_seq_len, float sm_scale,
+                           int32_t skip_single) {
+  const int32_t G = num_qo_heads / pool->num_kv_heads;
+  ExtendParams p;
+  p.k_cache = k_half(pool, layer);
+  p.v_cache = v_half(pool, layer);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_stride = q_row_stride;
+  p.out = static_cast<uint16_t*>(out);
+  p.page_table = page_table;
+  p.pt_stride = page_table_stride;
+  p.table_idx = table_idx;
+  p.prefix_lens = prefix_lens;
+  p.extend_lens = extend_lens;
+  p.cu_extend = cu_extend_lens;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.group = G;
+  p.page_size = pool->page_size;
+  p.num_mtiles = mtiles;
+  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
+  p.page_shift = page_shift_of(pool->page_size);
+  p.max_extend_len = max_extend_len;
+  p.max_seq_len = max_seq_len;
+  p.num_slots = static_cast<int32_t>(num_slots(pool));
+  p.scale_log2 = sm_scale * kLog2e;
+  p.skip_single = skip_single;
+  return p;
+}
+
+// Host-side checks of an extend call (and of the extend half of a mixed
+// call), checked mode included; sets the launch shape.
+msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                          int64_t q_row_stride, void* out, const int32_t* page_table,
+                          int32_t page_table_stride, const int32_t* table_idx,
+                          const int32_t* prefix_lens, const int32_t* extend_lens,
+                          const int32_t* cu_extend_lens, int32_t batch,
+                          int32_t total_extend_tokens, int32_t max_extend_len,
+                          int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                          bool* nothing_to_do, int64_t* mtiles_out, int* waves_out) {
+  *nothing_to_do = false;
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (batch < 0 || total_extend_tokens < 0 || max_extend_len < 0 || max_seq_len < 0)
+    return MSGL_ERR_SHAPE;
+  if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) {
+    *nothing_to_do = true;
+    return MSGL_OK;
+  }
+  if (!q || !out || !page_table || !table_idx || !prefix_lens || !extend_lens || !cu_extend_lens)
+    return MSGL_ERR_NULL;
+  st = check_attention_geometry(pool, num_qo_heads);
+  if (st != MSGL_OK) return st;
+  if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  const int32_t d = pool->head_dim;
+  if (q_row_stride < static_cast<int64_t>(num_qo_heads) * d || (q_row_stride % 8) != 0 ||
+      !aligned16(q) || !aligned16(out))
+    return MSGL_ERR_SHAPE;
+  if (max_extend_len > max_seq_len) return MSGL_ERR_SHAPE;
+  // extend addresses one (K or V, layer) sub-tensor with 32-bit byte offsets
+  if (half_elems(pool) * 2 >= (int64_t{1} << 32)) return MSGL_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f)) return MSGL_ERR_SHAPE;
+  if (page_table_stride < 1) return MSGL_ERR_SHAPE;
+  const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
+  if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
+  const int32_t G = num_qo_heads / pool->num_kv_heads;
+  const int waves = extend_waves();
+  *waves_out = waves;
+  const int64_t rows_per_tile = 32 * waves;
+  const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + rows_per_tile - 1) / rows_per_tile;
+  if (mtiles > 65535) return MSGL_ERR_UNSUPPORTED;  // grid z
+  *mtiles_out = mtiles;
+  st = check_device();
+  if (st != MSGL_OK) return st;
+  if (env_on("MSGL_CHECK")) {
+    std::vector<int32_t> ti, pl, el, cu;
+    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(pl, prefix_lens, batch) ||
+        !copy_to_host(el, extend_lens, batch) || !copy_to_host(cu, cu_extend_lens, batch + 1))
+      return MSGL_ERR_HIP;
+    if (cu[0] != 0 || cu[batch] != total_extend_tokens) return MSGL_ERR_RANGE;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (pl[b] < 0 || el[b] < 0 || el[b] > max_extend_len ||
+          static_cast<int64_t>(pl[b]) + el[b] > max_seq_len || cu[b + 1] - cu[b] != el[b])
+        return MSGL_ERR_RANGE;
+      st = check_row_pages(page_table, page_table_stride, ti[b], pl[b] + el[b], pool);
+      if (st != MSGL_OK) return st;
+    }
+  }
+  return MSGL_OK;
+}
+
 }  // namespace
 
 // A captured store_kv + decode: the instantiated HIP graph.
@@ -269,36 +409,9 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
       if (st != MSGL_OK) return st;
     }
   }
-  DecodeParams p;
-  p.k_cache = k_half(pool, layer);
-  p.v_cache = v_half(pool, layer);
-  p.q = static_cast<const uint16_t*>(q);
-  p.q_stride = q_row_stride;
-  p.out = static_cast<uint16_t*>(out);
-  p.page_table = page_table;
-  p.pt_stride = page_table_stride;
-  p.table_idx = table_idx;
-  p.seq_lens = seq_lens;
-  p.num_kv_heads = pool->num_kv_heads;
-  p.group = num_qo_heads / pool->num_kv_heads;
-  p.page_size = pool->page_size;
-  p.chunk = decode_chunk(batch, pool->num_kv_heads, max_seq_len);
-  p.max_chunks = static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + p.chunk - 1) / p.chunk);
-  if (p.max_chunks < 1) p.max_chunks = 1;
-  p.num_slots = static_cast<int32_t>(num_slots(pool));
-  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
-  p.page_shift = page_shift_of(pool->page_size);
-  p.max_seq_len = max_seq_len;
-  p.scale_log2 = sm_scale * kLog2e;
-  if (need > 0) {
-    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * (num_qo_heads + 1);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(ws);
-    p.ws_ml = reinterpret_cast<float*>(ws + ((units * d * 4 + 255) / 256) * 256);
-  } else {
-    p.ws_o = nullptr;
-    p.ws_ml = nullptr;
-  }
+  const DecodeParams p = decode_params(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                       table_idx, seq_lens, batch, num_qo_heads, max_seq_len,
+                                       sm_scale, need > 0 ? workspace : nullptr);
   return hip_status(launch_decode(p, d, batch, static_cast<hipStream_t>(stream)));
 }
 
@@ -310,71 +423,59 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
                               int32_t total_extend_tokens, int32_t max_extend_len,
                               int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
                               void* stream) {
-  msgl_status st = check_pool(pool, layer);
-  if (st != MSGL_OK) return st;
-  if (batch < 0 || total_extend_tokens < 0 || max_extend_len < 0 || max_seq_len < 0)
-    return MSGL_ERR_SHAPE;
-  if (batch == 0 || total_extend_tokens == 0 || max_extend_len == 0) return MSGL_OK;
-  if (!q || !out || !page_table || !table_idx || !prefix_lens || !extend_lens || !cu_extend_lens)
-    return MSGL_ERR_NULL;
-  st = check_attention_geometry(pool, num_qo_heads);
-  if (st != MSGL_OK) return st;
-  if (batch > 65535) return MSGL_ERR_UNSUPPORTED;
+  bool nothing = false;
+  int64_t mtiles = 0;
+  int waves = 8;
+  msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                 table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
+                                 total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
+                                 sm_scale, &nothing, &mtiles, &waves);
+  if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;
-  if (q_row_stride < static_cast<int64_t>(num_qo_heads) * d || (q_row_stride % 8) != 0 ||
-      !aligned16(q) || !aligned16(out))
-    return MSGL_ERR_SHAPE;
-  if (max_extend_len > max_seq_len) return MSGL_ERR_SHAPE;
-  // extend addresses one (K or V, layer) sub-tensor with 32-bit byte offsets
-  if (half_elems(pool) * 2 >= (int64_t{1} << 32)) return MSGL_ERR_UNSUPPORTED;
-  if (!(sm_scale > 0.f)) return MSGL_ERR_SHAPE;
-  if (page_table_stride < 1) return MSGL_ERR_SHAPE;
-  const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
-  if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
-  const int32_t G = num_qo_heads / pool->num_kv_heads;
-  const int waves = extend_waves();
-  const int64_t rows_per_tile = 32 * waves;
-  const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + rows_per_tile - 1) / rows_per_tile;
-  if (mtiles > 65535) return MSGL_ERR_UNSUPPORTED;  // grid z
-  st = check_device();
-  if (st != MSGL_OK) return st;
-  if (env_on("MSGL_CHECK")) {
-    std::vector<int32_t> ti, pl, el, cu;
-    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(pl, prefix_lens, batch) ||
-        !copy_to_host(el, extend_lens, batch) || !copy_to_host(cu, cu_extend_lens, batch + 1))
-      return MSGL_ERR_HIP;
-    if (cu[0] != 0 || cu[batch] != total_extend_tokens) return MSGL_ERR_RANGE;
-    for (int32_t b = 0; b < batch; ++b) {
-      if (pl[b] < 0 || el[b] < 0 || el[b] > max_extend_len ||
-          static_cast<int64_t>(pl[b]) + el[b] > max_seq_len || cu[b + 1] - cu[b] != el[b])
-        return MSGL_ERR_RANGE;
-      st = check_row_pages(page_table, page_table_stride, ti[b], pl[b] + el[b], pool);
-      if (st != MSGL_OK) return st;
-    }
-  }
-  ExtendParams p;
-  p.k_cache = k_half(pool, layer);
-  p.v_cache = v_half(pool, layer);
-  p.q = static_cast<const uint16_t*>(q);
-  p.q_stride = q_row_stride;
-  p.out = static_cast<uint16_t*>(out);
-  p.page_table = page_table;
-  p.pt_stride = page_table_stride;
-  p.table_idx = table_idx;
-  p.prefix_lens = prefix_lens;
-  p.extend_lens = extend_lens;
-  p.cu_extend = cu_extend_lens;
-  p.num_kv_heads = pool->num_kv_heads;
-  p.group = G;
-  p.page_size = pool->page_size;
-  p.num_mtiles = static_cast<int32_t>(mtiles);
-  p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
-  p.page_shift = page_shift_of(pool->page_size);
-  p.max_extend_len = max_extend_len;
-  p.max_seq_len = max_seq_len;
-  p.num_slots = static_cast<int32_t>(num_slots(pool));
-  p.scale_log2 = sm_scale * kLog2e;
+  const ExtendParams p = extend_params(pool, layer, q, q_row_stride, out, page_table,
+                                       page_table_stride, table_idx, prefix_lens, extend_lens,
+                                       cu_extend_lens, num_qo_heads, static_cast<int32_t>(mtiles),
+                                       max_extend_len, max_seq_len, sm_scale, 0);
   return hip_status(launch_extend(p, d, batch, waves, static_cast<hipStream_t>(stream)));
+}
+
+msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                             int64_t q_row_stride, void* out, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* table_idx,
+                             const int32_t* prefix_lens, const int32_t* extend_lens,
+                             const int32_t* cu_extend_lens, int32_t batch,
+                             int32_t total_extend_tokens, int32_t max_extend_len,
+                             int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  bool nothing = false;
+  int64_t mtiles = 0;
+  int waves = 8;
+  msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                 table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
+                                 total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
+                                 sm_scale, &nothing, &mtiles, &waves);
+  if (st != MSGL_OK || nothing) return st;
+  const int32_t d = pool->head_dim;
+  const size_t need =
+      msgl_paged_decode_workspace_size(batch, num_qo_heads, pool->num_kv_heads, d, max_seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSGL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MSGL_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // rows with one new token: split-KV decode and its merge
+  DecodeParams pd = decode_params(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                  table_idx, nullptr, batch, num_qo_heads, max_seq_len, sm_scale,
+                                  need > 0 ? workspace : nullptr);
+  pd.mixed_prefix = prefix_lens;
+  pd.mixed_extend = extend_lens;
+  pd.mixed_cu = cu_extend_lens;
+  st = hip_status(launch_decode(pd, d, batch, s));
+  if (st != MSGL_OK) return st;
+  // the other rows: causal extend
+  const ExtendParams pe = extend_params(pool, layer, q, q_row_stride, out, page_table,
+                                        page_table_stride, table_idx, prefix_lens, extend_lens,
+                                        cu_extend_lens, num_qo_heads, static_cast<int32_t>(mtiles),
+                                        max_extend_len, max_seq_len, sm_scale, 1);
+  return hip_status(launch_extend(pe, d, batch, waves, s));
 }
 
 msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,

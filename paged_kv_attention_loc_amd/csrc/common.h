@@ -169,6 +169,13 @@ struct DecodeParams {
   int32_t num_slots;
   uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
   float scale_log2;  // sm_scale * log2(e)
+  // mixed batches (all three set, seq_lens unused): request r is a decode
+  // row only when mixed_extend[r] == 1 -- the others belong to the extend
+  // kernel and are skipped; its length is mixed_prefix[r] + 1 and its q /
+  // out row is mixed_cu[r]
+  const int32_t* mixed_prefix;
+  const int32_t* mixed_extend;
+  const int32_t* mixed_cu;
 };
 
 struct ExtendParams {
@@ -193,6 +200,7 @@ struct ExtendParams {
   int32_t num_slots;
   uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
   float scale_log2;
+  int32_t skip_single;  // mixed batches: rows with one new token are left to decode
 };
 
 struct RopeParams {

@@ -84,12 +84,22 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
   const int G = p.group;
   const int Hq = p.num_kv_heads * G;
   // a length above max_seq_len breaks the caller's contract; clamp it so
-  // that no page_table entry past the row's bound is read
-  const int L = min(p.seq_lens[r], p.max_seq_len);
+  // that no page_table entry past the row's bound is read.  In a mixed
+  // batch only the rows with one new token are decoded here, and their
+  // q / out row is the request's first row of the batch.
+  int L;
+  int64_t io_row = r;
+  if (p.mixed_cu) {
+    if (p.mixed_extend[r] != 1) return;
+    L = min(p.mixed_prefix[r] + 1, p.max_seq_len);
+    io_row = p.mixed_cu[r];
+  } else {
+    L = min(p.seq_lens[r], p.max_seq_len);
+  }
 
   if (L <= 0) {  // padding row: zeros, no KV read
     if (s == 0) {
-      uint16_t* o = p.out + (static_cast<int64_t>(r) * Hq + g * G) * D;
+      uint16_t* o = p.out + (io_row * Hq + g * G) * D;
       for (int i = lane; i < G * LPT; i += 64) reinterpret_cast<uint4*>(o)[i] = make_uint4(0, 0, 0, 0);
     }
     return;
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
 
   // heads G .. GM-1 (a group size that is not a power of two) run on zero
   // queries and are never written
-  const uint16_t* qrow = p.q + static_cast<int64_t>(r) * p.q_stride + static_cast<int64_t>(g) * G * D;
+  const uint16_t* qrow = p.q + io_row * p.q_stride + static_cast<int64_t>(g) * G * D;
   for (int i = lane; i < GM * LPT; i += 64)
     q_lds[i] = (i < G * LPT) ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
 
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_k
   for (int h = 0; h < GM; ++h) l_tot[h] = wave_sum(l_run[h]);
   if (nch == 1) {
     if (lane < CPL) {
-      uint16_t* o = p.out + (static_cast<int64_t>(r) * Hq + g * G) * D + 2 * cw;
+      uint16_t* o = p.out + (io_row * Hq + g * G) * D + 2 * cw;
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h < G) {
@@ -277,7 +287,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int h = blockIdx.x;           // q head
   const int r = blockIdx.y;
   const int lane = threadIdx.x;
-  const int L = min(p.seq_lens[r], p.max_seq_len);
+  int L;
+  int64_t io_row = r;
+  if (p.mixed_cu) {
+    if (p.mixed_extend[r] != 1) return;
+    L = min(p.mixed_prefix[r] + 1, p.max_seq_len);
+    io_row = p.mixed_cu[r];
+  } else {
+    L = min(p.seq_lens[r], p.max_seq_len);
+  }
   if (L <= 0) return;
   const int nch = (L + p.chunk - 1) / p.chunk;
   if (nch <= 1) return;
@@ -321,7 +339,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     uint2 wv;
     wv.x = pack_bf16(acc.x * inv, acc.y * inv);
     wv.y = pack_bf16(acc.z * inv, acc.w * inv);
-    *reinterpret_cast<uint2*>(p.out + (static_cast<int64_t>(r) * Hq + h) * D + 4 * lane) = wv;
+    *reinterpret_cast<uint2*>(p.out + (io_row * Hq + h) * D + 4 * lane) = wv;
   }
 }
 

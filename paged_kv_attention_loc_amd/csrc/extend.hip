@@ -129,6 +129,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   // lengths above the host-side bounds break the caller's contract; clamp
   // them so that no page_table entry past the row's bound is read
   const int E = min(p.extend_lens[r], p.max_extend_len);
+  if (p.skip_single && E == 1) return;  // a decode row of a mixed batch
   const int M = E * G;
   const int m0 = mt * BM;
   if (m0 >= M) return;
