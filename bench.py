@@ -259,6 +259,63 @@ def alloc_stats(msgl, p, dev, iters=50):
     return {"requests": ph.batch, "new_tokens": ph.num_tokens, "avg_launch_us": round(float(np.mean(ts)), 2)}
 
 
+def mixed_stats(msgl, dev, iters=10):
+    """A mixed batch -- the 64 decode rows of the Llama-3-8B geometry batch
+    (lengths uniform in [512, 4096], seed 2) and 4 chunked-prefill pieces of
+    512 new tokens on 2048-token prefixes -- as one paged_mixed call and as
+    a decode call plus an extend call over the same rows."""
+    from workloads import build_case
+    rng = np.random.default_rng(2)
+    L = rng.integers(512, 4096, 64, endpoint=True)
+    P = [int(x) - 1 for x in L] + [2048] * 4
+    E = [1] * 64 + [512] * 4
+    wl = build_case(12, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    prefix_lens=P, extend_lens=E, device=dev)
+    ph = wl.phases[0]
+    p = Prepared(wl, ph, dev)
+    run_store(msgl, p)
+    dec = np.arange(64)
+    q_dec = p.q[torch.from_numpy(ph.cu_extend_lens[dec].astype(np.int64)).to(dev)].contiguous()
+    sl_dec = i32(np.asarray(P)[dec] + 1, dev)
+    ti_dec = i32(ph.table_idx[dec], dev)
+    ext = np.arange(64, 68)
+    first = int(ph.cu_extend_lens[64])
+    q_ext = p.q[first:].contiguous()
+    cu_ext = i32(ph.cu_extend_lens[64:] - first, dev)
+    ti_ext, pl_ext = i32(ph.table_idx[ext], dev), i32(ph.prefix_lens[ext], dev)
+    el_ext = i32(ph.extend_lens[ext], dev)
+    out = torch.empty_like(p.q)
+    out_dec, out_ext = torch.empty_like(q_dec), torch.empty_like(q_ext)
+    ws_dec = torch.empty(max(msgl.paged_decode_workspace_size(64, 32, 8, 128, p.max_len), 16),
+                         dtype=torch.uint8, device=dev)
+
+    def mixed():
+        msgl.paged_mixed(p.pool, wl.layer, p.q, p.pt, p.ti, p.pl, p.el, p.cu, p.max_ext, p.max_len,
+                         out=out, workspace=p.ws)
+
+    def separate():
+        msgl.paged_decode(p.pool, wl.layer, q_dec, p.pt, ti_dec, sl_dec, p.max_len, out=out_dec,
+                          workspace=ws_dec)
+        msgl.paged_extend(p.pool, wl.layer, q_ext, p.pt, ti_ext, pl_ext, el_ext, cu_ext, 512,
+                          p.max_len, out=out_ext)
+
+    res = {"decode_rows": 64, "extend_rows": 4, "extend_tokens": 2048}
+    for name, fn in (("mixed_call_us", mixed), ("separate_calls_us", separate)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        res[name] = round(float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3, 1)
+    del p, wl
+    return res
+
+
 def graph_vs_eager(msgl, dev, iters=300):
     """A small decode step -- store_kv of 8 new rows, then decode of 8
     requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
@@ -428,6 +485,8 @@ def main():
 
     log("device-side page allocation")
     alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
+    log("mixed decode + extend batch")
+    mixed = mixed_stats(msgl, dev)
     log("fused rotary embedding + store_kv (extend rows)")
     rope_stats = rope_store_stats(msgl, pe, dev)
     graph_stats = None
@@ -504,6 +563,7 @@ def main():
         "decode_graph": graph_stats,
         "rope_store_kv": rope_stats,
         "alloc_pages": alloc,
+        "mixed_batch": mixed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
