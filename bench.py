@@ -47,17 +47,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # since, the figure no longer describes the kernel and is reported as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_split_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "64ab301b1f7358b2dca5724b9878aadeb5b51c64453e04840e908b37dad1468c",
-                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758",
-                    "abi.hip": "8148f30c4df268ead72718e0d4cad2d62d7d99df50a7f1f341d65c82cf9cf4c9"},
-        "bytes": 653295840,
+        "sources": {"decode.hip": "b4ae3bce2f7c9085a9e4421b14c33ba5210c44b7ada3523ffe29658e4c019715",
+                    "common.h": "9c4558d3af57e4266079d0fe3027081cb051b1041a710da8726b650c7e2ef2f0",
+                    "abi.hip": "16ac49cce5a726b1f250d845f0ae65dbed6375d98354ad28bd9bed40283c6411"},
+        "bytes": 653306952,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
-        "sources": {"extend.hip": "90f01e7c86aacad1887710ae444a49137dcf66ca674b6597038a1606559468ca",
-                    "common.h": "11b4f59dd2b923deebbcdf42614ebab91cc37b7d9d211834409d8478411da758",
-                    "abi.hip": "8148f30c4df268ead72718e0d4cad2d62d7d99df50a7f1f341d65c82cf9cf4c9"},
-        "bytes": 240123648,
+        "sources": {"extend.hip": "6118559c6e09d760d8deba47685a82ecaabacde15a959630fba571489fecde33",
+                    "common.h": "9c4558d3af57e4266079d0fe3027081cb051b1041a710da8726b650c7e2ef2f0",
+                    "abi.hip": "16ac49cce5a726b1f250d845f0ae65dbed6375d98354ad28bd9bed40283c6411"},
+        "bytes": 239678496,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
 }
@@ -391,8 +391,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle work")
     ap.add_argument("--cold-iters", type=int, default=10)
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the small decode-graph comparison (keeps profiles to the step's kernels)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="skip the extra measurements (decode graphs, mixed batch, page allocation, "
+                         "fused rotary embedding), so that profiles see only the step's kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -483,14 +484,14 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    log("device-side page allocation")
-    alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
-    log("mixed decode + extend batch")
-    mixed = mixed_stats(msgl, dev)
-    log("fused rotary embedding + store_kv (extend rows)")
-    rope_stats = rope_store_stats(msgl, pe, dev)
-    graph_stats = None
-    if not args.no_graph:
+    alloc = mixed = rope_stats = graph_stats = None
+    if not args.step_only:
+        log("device-side page allocation")
+        alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
+        log("mixed decode + extend batch")
+        mixed = mixed_stats(msgl, dev)
+        log("fused rotary embedding + store_kv (extend rows)")
+        rope_stats = rope_store_stats(msgl, pe, dev)
         log("decode graph vs eager calls (small batch)")
         graph_stats = graph_vs_eager(msgl, dev)
 
