@@ -24,7 +24,8 @@
  *   - All pointers except the pool struct itself are device pointers.  The
  *     caller owns every buffer; the library allocates no device memory and
  *     keeps no state between calls other than a per-device architecture
- *     check.
+ *     check -- except the decode-graph objects, which the caller creates
+ *     and destroys explicitly.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream) and performs no host synchronisation, so calls are
  *     ordered by the stream: store_kv before the attention that reads it.
@@ -259,8 +260,10 @@ msgl_status msgl_alloc_pages(const int32_t* free_pages, int32_t* num_free, int32
  * smaller real batch are padded with out_loc = -1 and seq_lens = 0 (zeros
  * out, no KV read).  max_seq_len is the bound the grid is sized for; every
  * replayed seq_lens[r] must stay within it.
- *   graph_out : receives the new graph (host object owning a HIP graph
- *               executable; no device buffer is allocated by the library).
+ *   graph_out : receives the new graph, a host object owning a HIP graph
+ *               executable.  The library allocates no buffer for it; the
+ *               HIP runtime keeps the executable's own resources until
+ *               msgl_decode_graph_destroy.
  * Returns MSGL_ERR_UNSUPPORTED in checked mode (MSGL_CHECK=1), whose host
  * synchronisation cannot be captured, and MSGL_ERR_HIP when capture or
  * instantiation fails; *graph_out is then NULL.
