@@ -151,7 +151,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const int lim = P + ti;
   const bool wave_rows = m0 + w * 32 < M;  // does this wave own any row
 
-  const uint16_t* qp = p.q + static_cast<int64_t>(p.cu_extend[r] + ti) * p.q_stride +
+  // first token row of the request, kept in a register: the output
+  // stores could alias the array, so re-reading it would reload it each time
+  const int cu_r = p.cu_extend[r];
+  const uint16_t* qp = p.q + static_cast<int64_t>(cu_r + ti) * p.q_stride +
                        static_cast<int64_t>(g * G + hh) * D + hi * 8;
   bf16x8_t qop[KS];
 #pragma unroll
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       if (orow_m < M) {
         const int oti = orow_m / G;
         const int ohh = orow_m - oti * G;
-        uint16_t* dst = p.out + (static_cast<int64_t>(p.cu_extend[r] + oti) * Hq + g * G + ohh) * D + k * 8;
+        uint16_t* dst = p.out + (static_cast<int64_t>(cu_r + oti) * Hq + g * G + ohh) * D + k * 8;
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
       }
     }
