@@ -317,21 +317,25 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       bf16x8_t pop[4];
       constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
       auto probabilities = [&](float mref) {
-        lsum = 0.f;
+        // the row sum adds the bf16 values that the P.V product uses, in
+        // four independent partial sums (one per k-step) so that the dot2
+        // accumulations do not form one serial chain
+        float part[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           uint32_t wds[4];
+          part[kk] = 0.f;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const int e = 8 * (kk & 1) + 2 * e2;
             const float p0 = fast_exp2(fmaf(sc[kk >> 1][e], p.scale_log2, -mref));
             const float p1 = fast_exp2(fmaf(sc[kk >> 1][e + 1], p.scale_log2, -mref));
             wds[e2] = pack_bf16(p0, p1);
-            // the row sum adds the bf16 values that the P.V product uses
-            lsum = dot2_bf16(wds[e2], kOnes, lsum);
+            part[kk] = dot2_bf16(wds[e2], kOnes, part[kk]);
           }
           pop[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
         }
+        lsum = (part[0] + part[1]) + (part[2] + part[3]);
       };
       bool slow = m_run == -INFINITY;
       if (__builtin_amdgcn_ballot_w64(slow) == 0) {
