@@ -316,6 +316,94 @@ def mixed_stats(msgl, dev, iters=10):
     return res
 
 
+def other_workloads(msgl, dev, ext_iters=3, dec_iters=20):
+    """The two remaining workloads, each as store_kv then attention, timed
+    with HIP events on the launch stream (warm caches):
+      * chunked prefill: one 32768-token request as 8 extend chunks of 4096
+        over the growing prefix (32 q / 8 kv heads, d 128, ps 16, std 0.5);
+      * Qwen3-30B-A3B attention geometry decode: 32 q / 4 kv heads, d 128,
+        page_size 1, 256 requests with lognormal lengths (sum 824055).
+    """
+    from workloads import config_chunked_prefill, config_qwen3_moe_decode
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    res = {}
+    wl = config_chunked_prefill(device=dev)
+    preps = [Prepared(wl, ph, dev) for ph in wl.phases]
+    for p in preps:  # the pool holds every chunk's rows before timing
+        run_store(msgl, p)
+        run_extend(msgl, p)
+    torch.cuda.synchronize()
+    st_ms = np.zeros((ext_iters, len(preps)))
+    ex_ms = np.zeros((ext_iters, len(preps)))
+    for it in range(ext_iters):
+        marks = []
+        for p in preps:
+            e = [ev(), ev(), ev()]
+            e[0].record()
+            run_store(msgl, p)
+            e[1].record()
+            run_extend(msgl, p)
+            e[2].record()
+            marks.append(e)
+        torch.cuda.synchronize()
+        for c, e in enumerate(marks):
+            st_ms[it, c] = e[0].elapsed_time(e[1])
+            ex_ms[it, c] = e[1].elapsed_time(e[2])
+    fl = [extend_flops(wl, p.ph) for p in preps]
+    chunk_ms = np.median(ex_ms, axis=0)
+    tot_ms = float(chunk_ms.sum())
+    tf = sum(fl) / (tot_ms * 1e-3) / 1e12
+    res["chunked_prefill"] = {
+        "workload": "1 request of 32768 tokens as 8 extend chunks of 4096; 32q/8kv d128 ps16, std 0.5",
+        "algorithmic_flops": int(sum(fl)),
+        "extend_us_per_chunk": [round(x * 1e3, 1) for x in chunk_ms],
+        "TFLOP/s_per_chunk": [round(f / (m * 1e-3) / 1e12, 1) for f, m in zip(fl, chunk_ms)],
+        "extend_total_us": round(tot_ms * 1e3, 1),
+        "TFLOP/s": round(tf, 2),
+        "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "store_kv_avg_us": round(float(st_ms.mean()) * 1e3, 2),
+        "store_kv_GBs": round(store_bytes(wl, preps[0].ph.num_tokens) / (float(st_ms.mean()) * 1e-3) / 1e9, 1),
+    }
+    del preps, wl
+    torch.cuda.empty_cache()
+
+    wl = config_qwen3_moe_decode(device=dev)
+    p = Prepared(wl, wl.phases[0], dev)
+    for _ in range(3):
+        run_store(msgl, p)
+        run_decode(msgl, p)
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(dec_iters):
+        e = [ev(), ev(), ev()]
+        e[0].record()
+        run_store(msgl, p)
+        e[1].record()
+        run_decode(msgl, p)
+        e[2].record()
+        marks.append(e)
+    torch.cuda.synchronize()
+    st = np.array([e[0].elapsed_time(e[1]) for e in marks])
+    dm = np.array([e[1].elapsed_time(e[2]) for e in marks])
+    db = decode_bytes(wl, p.ph)
+    gbs = db / (float(dm.mean()) * 1e-3) / 1e9
+    res["qwen3_moe_decode"] = {
+        "workload": "32q/4kv d128 ps1, 256 requests, lognormal lengths (sum 824055), slots scattered",
+        "algorithmic_bytes": db,
+        "decode_avg_us": round(float(dm.mean()) * 1e3, 1),
+        "decode_median_us": round(float(np.median(dm)) * 1e3, 1),
+        "GB/s": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "store_kv_avg_us": round(float(st.mean()) * 1e3, 2),
+    }
+    del p, wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def graph_vs_eager(msgl, dev, iters=300):
     """A small decode step -- store_kv of 8 new rows, then decode of 8
     requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
@@ -393,7 +481,8 @@ def main():
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--step-only", action="store_true",
                     help="skip the extra measurements (decode graphs, mixed batch, page allocation, "
-                         "fused rotary embedding), so that profiles see only the step's kernels")
+                         "fused rotary embedding, the other two workloads), so that profiles see "
+                         "only the step's kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -484,7 +573,7 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    alloc = mixed = rope_stats = graph_stats = None
+    alloc = mixed = rope_stats = graph_stats = others = None
     if not args.step_only:
         log("device-side page allocation")
         alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
@@ -494,6 +583,8 @@ def main():
         rope_stats = rope_store_stats(msgl, pe, dev)
         log("decode graph vs eager calls (small batch)")
         graph_stats = graph_vs_eager(msgl, dev)
+        log("chunked 32k prefill and the Qwen3-30B-A3B-geometry decode")
+        others = other_workloads(msgl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -565,6 +656,7 @@ def main():
         "rope_store_kv": rope_stats,
         "alloc_pages": alloc,
         "mixed_batch": mixed,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
