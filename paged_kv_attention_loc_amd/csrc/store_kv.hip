@@ -33,32 +33,54 @@ struct VecType<2> {
   using T = uint16_t;
 };
 
-template <int VEC>
+// Grid: x = groups of U tokens, y = blocks of blockDim.x pieces of a
+// token's K row followed by its V row (blockDim.x: the two rows' pieces
+// rounded up to whole waves, at most 256).  A thread owns one piece position and copies it
+// for the U tokens of its group: the U loads are all issued before the
+// first store, so each thread keeps U independent reads in flight.  The
+// slots are block-uniform (scalar loads).
+template <int VEC, int U>
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   using V = typename VecType<VEC>::T;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int ppr = p.pieces_per_row;
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; it < p.num_items;
-       it += stride) {
-    const int64_t t = it / (2 * ppr);
-    const int rem = static_cast<int>(it - t * 2 * ppr);
-    const int half = rem >= ppr;  // 0 = K, 1 = V
-    const int piece = rem - half * ppr;
-    const int32_t slot = p.out_loc[t];
-    if (slot < 0 || slot >= p.num_slots) continue;  // padding row (or outside the pool)
-    const uint8_t* src = (half ? p.v + t * p.v_stride_bytes : p.k + t * p.k_stride_bytes) +
-                         static_cast<int64_t>(piece) * VEC;
-    uint8_t* dst = (half ? p.v_cache : p.k_cache) + static_cast<int64_t>(slot) * p.row_bytes +
-                   static_cast<int64_t>(piece) * VEC;
-    if constexpr (VEC == 16) {
-      // nontemporal on both sides: the new rows are read once here, and
-      // written through rather than left as dirty lines that a later,
-      // bandwidth-bound kernel would have to write back
-      typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src)),
-                                  reinterpret_cast<u32x4v*>(dst));
-    } else {
-      *reinterpret_cast<V*>(dst) = *reinterpret_cast<const V*>(src);
+  const int j = static_cast<int>(blockIdx.y * blockDim.x + threadIdx.x);
+  if (j >= 2 * ppr) return;
+  const int half = j >= ppr;  // 0 = K, 1 = V
+  const int64_t piece_off = static_cast<int64_t>(j - half * ppr) * VEC;
+  const uint8_t* src = (half ? p.v : p.k) + piece_off;
+  const int64_t src_stride = half ? p.v_stride_bytes : p.k_stride_bytes;
+  uint8_t* dst = (half ? p.v_cache : p.k_cache) + piece_off;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * U;
+  int32_t slot[U];
+  V val[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t t = t0 + u;
+    slot[u] = t < p.num_tokens ? p.out_loc[t] : -1;
+    // padding rows (out_loc < 0) and slots outside the pool are skipped
+    if (slot[u] >= 0 && slot[u] < p.num_slots) {
+      if constexpr (VEC == 16) {
+        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+        val[u] = __builtin_bit_cast(V, __builtin_nontemporal_load(
+                                           reinterpret_cast<const u32x4v*>(src + t * src_stride)));
+      } else {
+        val[u] = *reinterpret_cast<const V*>(src + t * src_stride);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (slot[u] >= 0 && slot[u] < p.num_slots) {
+      uint8_t* d = dst + static_cast<int64_t>(slot[u]) * p.row_bytes;
+      if constexpr (VEC == 16) {
+        // nontemporal on both sides: the new rows are read once here, and
+        // written through rather than left as dirty lines that a later,
+        // bandwidth-bound kernel would have to write back
+        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, val[u]), reinterpret_cast<u32x4v*>(d));
+      } else {
+        *reinterpret_cast<V*>(d) = val[u];
+      }
     }
   }
 }
@@ -84,20 +106,38 @@ static int grid_for(int64_t items) {
   return static_cast<int>(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
 }
 
+// Tokens per thread: 4 once there are enough tokens to fill the chip with
+// such groups, else 1 (small steps are latency-bound: more, smaller
+// workgroups finish sooner).
+constexpr int kStoreGroupMin = 2048;
+
+template <int VEC>
+static void launch_store_t(const StoreParams& p, hipStream_t stream) {
+  const int pieces = 2 * p.pieces_per_row;
+  const int tb = pieces >= 256 ? 256 : (pieces + 63) / 64 * 64;
+  const int yb = (pieces + tb - 1) / tb;
+  if (p.num_tokens >= kStoreGroupMin) {
+    const dim3 grid((p.num_tokens + 3) / 4, yb);
+    hipLaunchKernelGGL((store_kv_kernel<VEC, 4>), grid, dim3(tb), 0, stream, p);
+  } else {
+    const dim3 grid(p.num_tokens > 0 ? p.num_tokens : 1, yb);
+    hipLaunchKernelGGL((store_kv_kernel<VEC, 1>), grid, dim3(tb), 0, stream, p);
+  }
+}
+
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream) {
-  const dim3 grid(grid_for(p.num_items)), block(256);
   switch (vec_bytes) {
     case 16:
-      hipLaunchKernelGGL(store_kv_kernel<16>, grid, block, 0, stream, p);
+      launch_store_t<16>(p, stream);
       break;
     case 8:
-      hipLaunchKernelGGL(store_kv_kernel<8>, grid, block, 0, stream, p);
+      launch_store_t<8>(p, stream);
       break;
     case 4:
-      hipLaunchKernelGGL(store_kv_kernel<4>, grid, block, 0, stream, p);
+      launch_store_t<4>(p, stream);
       break;
     default:
-      hipLaunchKernelGGL(store_kv_kernel<2>, grid, block, 0, stream, p);
+      launch_store_t<2>(p, stream);
       break;
   }
   return hipGetLastError();
