@@ -141,6 +141,32 @@ def test_store_kv_strided_views_and_padding():
     assert np.array_equal(bits(dev.pool), ref)
 
 
+@pytest.mark.parametrize("hkv,d,pad", [(8, 128, 0), (4, 128, 4), (2, 64, 2)])
+def test_store_kv_many_rows_ragged(hkv, d, pad):
+    # 2051 rows: enough for the four-tokens-per-lane launch, and not a
+    # multiple of four; every fifth row padded; the row pad (in elements)
+    # forces 16-, 8- and 4-byte pieces
+    wl = build_case(103 + pad, num_qo_heads=hkv, num_kv_heads=hkv, head_dim=d, page_size=16,
+                    prefix_lens=[0, 5, 700], extend_lens=[1000, 1048, 3])
+    ph = wl.phases[0]
+    T = ph.num_tokens
+    assert T == 2051
+
+    def padded(x):
+        buf = torch.zeros((T, hkv * d + pad), dtype=torch.bfloat16)
+        buf[:, :hkv * d] = x.reshape(T, hkv * d)
+        return buf.cuda().as_strided((T, hkv, d), (hkv * d + pad, d, 1))
+
+    loc = ph.out_loc.copy()
+    loc[::5] = -1
+    dev = Dev(wl)
+    _say(f"store_kv {T} rows, hkv={hkv} d={d} row pad {pad}")
+    msgl.store_kv(dev.pool, 0, padded(ph.k), padded(ph.v), _i32(loc))
+    torch.cuda.synchronize()
+    ref = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), loc)
+    assert np.array_equal(bits(dev.pool), ref)
+
+
 @pytest.mark.parametrize("ps", [1, 2, 16, 64])
 def test_gather_bit_exact(ps):
     wl = build_case(103 + ps, num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=ps,
