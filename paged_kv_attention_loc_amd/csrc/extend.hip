@@ -40,6 +40,10 @@
 //     the S^T accumulator registers hold the keys -- so P^T feeds the
 //     second MFMA straight from registers.  Per-lane read addresses are
 //     computed once; the tile, stage and block parts are immediates;
+//   * q is scaled by scale*log2(e) and rounded to bf16 once per workgroup,
+//     and a ninth k-step per 32-key block (a constant ones operand against
+//     -m as a bf16 pair) subtracts the running maximum inside the MFMA, so
+//     a probability is one v_exp_f32 of the accumulator;
 //   * the running maximum only moves when a row's new maximum exceeds it by
 //     more than 2^8 in exp2 terms, so the O rescale is rare; masking runs
 //     only on tiles that cross a row's causal limit.
@@ -156,9 +160,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const int cu_r = p.cu_extend[r];
   const uint16_t* qp = p.q + static_cast<int64_t>(cu_r + ti) * p.q_stride +
                        static_cast<int64_t>(g * G + hh) * D + hi * 8;
+  // q is scaled by scale*log2(e) and rounded once to bf16, so that the
+  // scores leave the MFMA in log2 units, ready for exp2
   bf16x8_t qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * p.scale_log2);
+    qop[ks] = x;
+  }
 
   const int wrow0 = min(m0 + w * 32, M - 1);
   const int wrow1 = min(m0 + w * 32 + 31, M - 1);
@@ -211,8 +222,20 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+  // m_run: the running maximum of the (log2-unit) scores of this lane's
+  // query column, kept exactly equal to a bf16 pair sum hi + lo.  A ninth
+  // k-step of S^T = K Q^T adds -m_run to every score: its A operand holds
+  // ones in k slots 0 and 1 (lanes of the first half, zeros elsewhere) and
+  // its B operand -hi and -lo in the same slots, so the softmax needs no
+  // per-score subtraction.  Before the first tile the offset is zero.
   float m_run = -INFINITY;
   float l_run = 0.f;
+  bf16x8_t a_ones, b_negm;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a_ones[e] = static_cast<__bf16>((hi == 0 && e < 2) ? 1.f : 0.f);
+    b_negm[e] = static_cast<__bf16>(0.f);
+  }
 
   // prologue: tile 0 in stage 0; tile 1 on its way to stage 1; tile 2's
   // entries in flight (the barrier's fence waits for the DMA)
@@ -275,22 +298,26 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       };
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks]);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ones, b_negm, sc[0], 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[0], 0, 0, 0);
         ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks] + 32 * ROWB);
       }
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ones, b_negm, sc[1], 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[1], 0, 0, 0);
         if (ks < 4) va[ks] = load_va(0, ks);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -305,18 +332,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
           for (int e = 0; e < 16; ++e)
             if (32 * kb + 8 * (e >> 2) + (e & 3) > lim_rel) sc[kb][e] = -INFINITY;
       }
-      // ---- online softmax in the log2 domain; the scale (> 0) is folded
-      // into one fma per score.  Fast path: exponentiate against the
-      // running maximum as it stands; that is exact softmax arithmetic as
+      // ---- online softmax in the log2 domain.  The scores already are
+      // s - m_off (m_off: m_run, or 0 before the first tile).  Fast path:
+      // exponentiate them as they stand; that is exact softmax arithmetic as
       // long as no probability exceeds 2^8, which a lane row sum of at most
       // 2^8 guarantees.  Otherwise (and on a wave's first tile, whose
       // maximum is still -inf) the tile maximum is taken, the running
       // maximum moves if the tile's exceeds it by more than 2^8, and the
-      // probabilities are recomputed.
+      // probabilities are recomputed against the new maximum.
       float lsum = 0.f;
       bf16x8_t pop[4];
       constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
-      auto probabilities = [&](float mref) {
+      auto probabilities = [&](float delta) {  // p = 2^(score - delta)
         // the row sum adds the bf16 values that the P.V product uses, in
         // four independent partial sums (one per k-step) so that the dot2
         // accumulations do not form one serial chain
@@ -328,8 +355,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const int e = 8 * (kk & 1) + 2 * e2;
-            const float p0 = fast_exp2(fmaf(sc[kk >> 1][e], p.scale_log2, -mref));
-            const float p1 = fast_exp2(fmaf(sc[kk >> 1][e + 1], p.scale_log2, -mref));
+            const float p0 = fast_exp2(sc[kk >> 1][e] - delta);
+            const float p1 = fast_exp2(sc[kk >> 1][e + 1] - delta);
             wds[e2] = pack_bf16(p0, p1);
             part[kk] = dot2_bf16(wds[e2], kOnes, part[kk]);
           }
@@ -339,21 +366,36 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       };
       bool slow = m_run == -INFINITY;
       if (__builtin_amdgcn_ballot_w64(slow) == 0) {
-        probabilities(m_run);
+        probabilities(0.f);
         slow = !(lsum <= kSumLimit);  // also catches inf
       }
       if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+        const float m_off = m_run == -INFINITY ? 0.f : m_run;
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-        mx = xor32_max(mx) * p.scale_log2;
+        mx = xor32_max(mx) + m_off;
         const bool move = mx > m_run + kMaxSlack;
-        const float mnew = move ? mx : m_run;
+        // a new maximum is rounded to a bf16 pair sum, which the offset
+        // k-step then subtracts exactly
+        float mnew = m_run;
+        __bf16 mh = static_cast<__bf16>(0.f), ml = static_cast<__bf16>(0.f);
+        if (move) {
+          mh = static_cast<__bf16>(mx);
+          ml = static_cast<__bf16>(mx - static_cast<float>(mh));
+          mnew = static_cast<float>(mh) + static_cast<float>(ml);
+        }
         const float alpha = fast_exp2(m_run - mnew);
-        m_run = mnew;
-        probabilities(m_run);
+        probabilities(mnew - m_off);
+        if (move) {
+          m_run = mnew;
+          if (hi == 0) {
+            b_negm[0] = -mh;
+            b_negm[1] = -ml;
+          }
+        }
         // the rescale is skipped when no row of the wave moved its maximum
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
           l_run *= alpha;
