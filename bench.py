@@ -54,10 +54,10 @@ MEASURED_TRAFFIC = {
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
     "extend": {
-        "sources": {"extend.hip": "1349b0ec9558a5d3ac4c753dcd63c69f04d2002442e84a4273d3843e2887e1c8",
+        "sources": {"extend.hip": "2bca8344bcd68c94963b5813a7a7a3f789b7b6028378fcc5f29c4e337af488eb",
                     "common.h": "9c4558d3af57e4266079d0fe3027081cb051b1041a710da8726b650c7e2ef2f0",
                     "abi.hip": "16ac49cce5a726b1f250d845f0ae65dbed6375d98354ad28bd9bed40283c6411"},
-        "bytes": 240713536,
+        "bytes": 239759520,
         "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
     },
 }
