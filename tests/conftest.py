@@ -13,5 +13,5 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on a GPU box; here they are deselected by -m "not gpu".
+    # tests marked gpu need an MI355X; on a machine without one, select -m "not gpu"
     pass
