@@ -9,6 +9,7 @@ from .paged_kv import (  # noqa: F401
     float_to_bf16_bits,
     gather_kv,
     paged_attention,
+    paged_attention_blocked,
     paged_decode,
     store_kv,
     token_slots,

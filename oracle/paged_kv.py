@@ -51,6 +51,7 @@ __all__ = [
     "token_slots",
     "gather_kv",
     "paged_attention",
+    "paged_attention_blocked",
     "paged_decode",
 ]
 
@@ -210,12 +211,77 @@ def paged_attention(pool: np.ndarray, layer: int, q: np.ndarray, page_table: np.
     return out
 
 
+def paged_attention_blocked(pool: np.ndarray, layer: int, q: np.ndarray, page_table: np.ndarray,
+                            table_idx: np.ndarray, prefix_lens: np.ndarray,
+                            extend_lens: np.ndarray, sm_scale: Optional[float] = None,
+                            dtype=np.float32, only_tokens: Optional[Iterable[int]] = None,
+                            block: int = 256) -> np.ndarray:
+    """The same causal GQA attention as ``paged_attention``, evaluated for a
+    block of up to ``block`` query tokens of one request and one kv head at
+    a time, in matrix form:
+
+        S = sm_scale * Q K^T          (rows: the block's (token, q head) pairs)
+        S[row, j] = -inf  for every key j after the row's position a
+        W = exp(S - rowmax(S));  out = (W V) / rowsum(W)
+
+    Masked keys get weight exp(-inf) = 0 exactly, so each row is the
+    per-row definition above; only the summation order inside the matrix
+    products differs.  This is the form that finishes in seconds at the
+    full workload sizes (tens of thousands of keys per row).  Arguments and
+    result are those of ``paged_attention``.
+    """
+    pool = _as_bits(pool)
+    qb = _as_bits(q)
+    two, nl, npg, ps, hkv, d = pool.shape
+    T, hq, dq = qb.shape
+    assert dq == d and hq % hkv == 0 and block >= 1
+    G = hq // hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    P = np.asarray(prefix_lens, dtype=np.int64)
+    E = np.asarray(extend_lens, dtype=np.int64)
+    assert len(P) == len(E) == len(table_idx)
+    cu = np.concatenate([[0], np.cumsum(E)])
+    assert cu[-1] == T
+    wanted = None if only_tokens is None else np.unique(np.asarray(list(only_tokens), np.int64))
+    out = np.full((T, hq, d), np.nan, dtype=dtype)
+    scale = dtype(sm_scale)
+    for r in range(len(P)):
+        if E[r] == 0:
+            continue
+        rows = np.arange(cu[r], cu[r + 1], dtype=np.int64)
+        if wanted is not None:
+            rows = rows[np.isin(rows, wanted)]
+        if len(rows) == 0:
+            continue
+        L = int(P[r] + E[r])
+        kb, vb = gather_kv(pool, layer, page_table, int(table_idx[r]), L)
+        for g in range(hkv):
+            Kg = np.ascontiguousarray(bf16_bits_to_float(kb[:, g, :], dtype))  # (L, d)
+            Vg = np.ascontiguousarray(bf16_bits_to_float(vb[:, g, :], dtype))
+            for b0 in range(0, len(rows), block):
+                blk = rows[b0:b0 + block]
+                a = P[r] + (blk - cu[r])  # absolute positions of the block's tokens
+                n = int(a.max()) + 1
+                Q = bf16_bits_to_float(qb[blk, g * G:(g + 1) * G, :], dtype).reshape(-1, d)
+                S = (Q @ Kg[:n].T) * scale  # (len(blk)*G, n)
+                pos = np.repeat(a, G)
+                S[np.arange(n)[None, :] > pos[:, None]] = -np.inf
+                S -= S.max(axis=1, keepdims=True)
+                np.exp(S, out=S)
+                o = (S @ Vg[:n]) / S.sum(axis=1, keepdims=True)
+                out[blk, g * G:(g + 1) * G] = o.reshape(len(blk), G, d)
+    return out
+
+
 def paged_decode(pool: np.ndarray, layer: int, q: np.ndarray, page_table: np.ndarray,
                  table_idx: np.ndarray, seq_lens: np.ndarray, sm_scale: Optional[float] = None,
-                 dtype=np.float32, only_tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+                 dtype=np.float32, only_tokens: Optional[Iterable[int]] = None,
+                 blocked: bool = False) -> np.ndarray:
     """Decode: one new token per request whose row is already stored, so
     seq_len counts it; the query attends to all seq_len keys.  A request
-    with seq_len 0 (a padding row) returns zeros."""
+    with seq_len 0 (a padding row) returns zeros.  ``blocked`` evaluates it
+    with ``paged_attention_blocked`` (same definition, matrix form)."""
     L = np.asarray(seq_lens, dtype=np.int64)
     qb = _as_bits(q)
     B = len(L)
@@ -228,9 +294,10 @@ def paged_decode(pool: np.ndarray, layer: int, q: np.ndarray, page_table: np.nda
         if only_tokens is not None:
             keep = set(int(t) for t in only_tokens)
             sub_only = [j for j, r in enumerate(idx) if int(r) in keep]
-        sub = paged_attention(pool, layer, qb[idx], page_table, np.asarray(table_idx)[idx],
-                              L[idx] - 1, np.ones(len(idx), np.int64), sm_scale, dtype,
-                              only_tokens=sub_only)
+        attend = paged_attention_blocked if blocked else paged_attention
+        sub = attend(pool, layer, qb[idx], page_table, np.asarray(table_idx)[idx],
+                     L[idx] - 1, np.ones(len(idx), np.int64), sm_scale, dtype,
+                     only_tokens=sub_only)
         out[idx] = sub
         if only_tokens is not None:
             keep = set(int(t) for t in only_tokens)

@@ -82,6 +82,13 @@ def test_p1_dense_contiguous(hq, hkv, d, ps, P, E, layout):
     got64 = oracle.paged_attention(pool, 0, Qb, pt, [1], [P], [E], dtype=np.float64)
     assert np.abs(got64 - ref).max() <= 1e-10
     assert np.abs(got32 - ref).max() <= 1e-5
+    # the blocked (matrix) form, with blocks that split the query rows
+    for block in (1, 7, 256):
+        b32 = oracle.paged_attention_blocked(pool, 0, Qb, pt, [1], [P], [E], block=block)
+        b64 = oracle.paged_attention_blocked(pool, 0, Qb, pt, [1], [P], [E], dtype=np.float64,
+                                             block=block)
+        assert np.abs(b64 - ref).max() <= 1e-10
+        assert np.abs(b32 - ref).max() <= 1e-5
 
 
 def _brute(pool, layer, q, page_table, table_idx, P, E, sm_scale):
@@ -149,6 +156,9 @@ def test_p2_brute_force_random_tiny(seed):
     assert np.abs(got - ref).max() <= 1e-9
     got32 = oracle.paged_attention(pool, 0, q, wl.page_table, ph.table_idx, P, E)
     assert np.abs(got32 - ref).max() <= 1e-5
+    blk = oracle.paged_attention_blocked(pool, 0, q, wl.page_table, ph.table_idx, P, E,
+                                         dtype=np.float64, block=2)
+    assert np.abs(blk - ref).max() <= 1e-9
 
 
 def _stored_case(seed=21, **kw):
@@ -237,11 +247,13 @@ def test_p6_uniform_weights_closed_form():
     pt = pages[None, :].astype(np.int32)
     Qb = np.zeros((E, hq, d), np.uint16)
     got = oracle.paged_attention(pool, 0, Qb, pt, [0], [P], [E])
+    blk = oracle.paged_attention_blocked(pool, 0, Qb, pt, [0], [P], [E], block=16)
     for i in range(E):
         a = P + i
         counts = np.array([len(range(c, a + 1, d)) for c in range(d)], np.float64)
         expect = counts / (a + 1)
         assert np.abs(got[i] - expect[None, :]).max() <= 1e-6
+        assert np.abs(blk[i] - expect[None, :]).max() <= 1e-6
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
@@ -270,17 +282,19 @@ def test_p7_boundary_probes(dtype):
         mirror_K[a, :, i] = 64.0
     for KK, kind in ((leak_K, "leak"), (mirror_K, "mirror")):
         pool = _place_contiguous(oracle.float_to_bf16_bits(KK), Vb, ps, pages, npg)
-        got = oracle.paged_attention(pool, 0, Qb, pt, [0], [P], [E], dtype=dtype)
-        for i in range(E):
-            a = P + i
-            if kind == "leak":
-                expect = Vw[: a + 1, 0].mean(axis=0)
-                assert np.abs(got[i] - expect[None]).max() <= 1e-5
-            else:
-                if dtype == np.float32:
-                    assert np.array_equal(got[i], np.repeat(Vw[a:a + 1, 0], hq, 0).astype(dtype))
+        for attend in (oracle.paged_attention,
+                       lambda *a, **k: oracle.paged_attention_blocked(*a, block=5, **k)):
+            got = attend(pool, 0, Qb, pt, [0], [P], [E], dtype=dtype)
+            for i in range(E):
+                a = P + i
+                if kind == "leak":
+                    expect = Vw[: a + 1, 0].mean(axis=0)
+                    assert np.abs(got[i] - expect[None]).max() <= 1e-5
                 else:
-                    assert np.abs(got[i] - Vw[a, 0][None]).max() <= 1e-200
+                    if dtype == np.float32:
+                        assert np.array_equal(got[i], np.repeat(Vw[a:a + 1, 0], hq, 0).astype(dtype))
+                    else:
+                        assert np.abs(got[i] - Vw[a, 0][None]).max() <= 1e-200
 
 
 def test_p8_chunked_equals_one_shot():
@@ -417,6 +431,30 @@ def test_golden_hand_example():
     assert np.abs(oute - np.array(g["extend"]["expected"])).max() <= 1e-12
 
 
+@pytest.mark.parametrize("seed", [81, 82])
+def test_blocked_form_matches_row_form(seed):
+    # the two evaluations of one definition, on ragged requests with
+    # several blocks each, a shared prefix and sampled rows
+    wl = build_case(seed, num_qo_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                    prefix_lens=[64, 64, 64], extend_lens=[70, 1, 33], shared_prefix=True)
+    ph = wl.phases[0]
+    pool = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
+    args = (pool, 0, bits(ph.q), wl.page_table, ph.table_idx, ph.prefix_lens, ph.extend_lens)
+    row = oracle.paged_attention(*args, dtype=np.float64)
+    blk = oracle.paged_attention_blocked(*args, dtype=np.float64, block=16)
+    assert np.abs(row - blk).max() <= 1e-12
+    some = [0, 5, 69, 70, 71, 103]
+    part = oracle.paged_attention_blocked(*args, dtype=np.float64, block=3, only_tokens=some)
+    assert np.abs(part[some] - row[some]).max() <= 1e-12
+    others = np.setdiff1d(np.arange(ph.num_tokens), some)
+    assert np.all(np.isnan(part[others]))
+    dec = oracle.paged_decode(pool, 0, bits(ph.q)[:3], wl.page_table, ph.table_idx,
+                              np.array([10, 0, 100]), dtype=np.float64)
+    decb = oracle.paged_decode(pool, 0, bits(ph.q)[:3], wl.page_table, ph.table_idx,
+                               np.array([10, 0, 100]), dtype=np.float64, blocked=True)
+    assert np.abs(dec - decb).max() <= 1e-12 and np.all(decb[1] == 0)
+
+
 def test_decode_padding_row_is_zero():
     wl = build_case(71, num_qo_heads=4, num_kv_heads=1, head_dim=64, page_size=16,
                     prefix_lens=[20, 7], extend_lens=[1, 1])
@@ -438,6 +476,11 @@ def test_bf16_rounding_helpers():
     assert back[0] == 1.0 and back[1] == -2.5
     assert back[2] == 1.0  # tie -> even
     assert back[3] == 1.0 + 4 * 2 ** -8  # tie -> even (up)
-    assert np.isinf(oracle.bf16_bits_to_float(oracle.float_to_bf16_bits(np.float32(3.4e38)))) or True
+    # 3.4e38 lies above the midpoint between the largest finite bf16
+    # (0x7F7F, about 3.39e38) and 2^128, so round-to-nearest-even overflows
+    # to +inf (0x7F80); the largest finite bf16 itself stays put
+    assert oracle.float_to_bf16_bits(np.float32(3.4e38)) == 0x7F80
+    assert np.isposinf(oracle.bf16_bits_to_float(oracle.float_to_bf16_bits(np.float32(3.4e38))))
+    assert oracle.float_to_bf16_bits(oracle.bf16_bits_to_float(np.uint16(0x7F7F))) == 0x7F7F
     t = torch.tensor(x).to(torch.bfloat16)
     assert np.array_equal(bits(t)[:5], b[:5])
