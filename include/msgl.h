@@ -174,9 +174,9 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
 
 /*
  * rope_store_kv: rotary position embedding of this step's new rows, fused
- * with store_kv ("Code Notes: mini-sglang", section "Layers", get_rope --
- * rotary position embeddings; Engine Layer table, BaseKVCachePool row for
- * the store).  For t < num_tokens, with p = positions[t]:
+ * with store_kv ("Code Structure", section Model Layers, get_rope --
+ * rotary position embeddings; "Code Notes: mini-sglang", Engine Layer
+ * table, BaseKVCachePool row for the store).  For t < num_tokens, with p = positions[t]:
  *   q[t, h, :] <- rope(q[t, h, :], p) in place, for every q head h;
  *   K[layer] slot out_loc[t] <- rope(k[t], p), V[layer] slot <- v[t]
  *   (rows with out_loc[t] < 0 store nothing; q is still rotated).

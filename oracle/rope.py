@@ -3,8 +3,9 @@ INFRASTRUCTURE (imported only by the tests; the product library never uses
 it and shares no code with it).
 
 The pages list rotary position embeddings (RoPE) among the model layers
-("Code Notes: mini-sglang", section "Layers", the get_rope / set_rope_device
-entry, and RotaryConfig among the model configuration classes) without
+("Code Structure", section Model Layers, the get_rope / set_rope_device
+entry; section Model Definitions, RotaryConfig among the model configuration
+classes) without
 stating the formula.  The reading taken is the standard rotary embedding:
 channel i < d/2 of a head is paired with channel i + d/2 (the half-split
 pairing of the Llama family the pages' model list names), and the pair at

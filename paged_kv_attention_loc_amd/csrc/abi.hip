@@ -109,21 +109,26 @@ int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_se
   return static_cast<int32_t>(c);
 }
 
+// Checked mode reads device metadata on the caller's stream, after the work
+// already queued there (which may be what wrote it), and waits for it.
 template <typename T>
-bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
   dst.resize(n);
   if (n == 0) return true;
-  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
 }
 
 // Checked mode: the page ids that tokens 0 .. len-1 of a row would read.
 msgl_status check_row_pages(const int32_t* page_table, int64_t stride, int32_t row, int32_t len,
-                            const msgl_kv_pool* pool) {
+                            const msgl_kv_pool* pool, hipStream_t stream) {
   if (row < 0) return MSGL_ERR_RANGE;
   if (len <= 0) return MSGL_OK;
   const int64_t npg = (len + pool->page_size - 1) / pool->page_size;
   std::vector<int32_t> ids;
-  if (!copy_to_host(ids, page_table + static_cast<int64_t>(row) * stride, static_cast<size_t>(npg)))
+  if (!copy_to_host(ids, page_table + static_cast<int64_t>(row) * stride, static_cast<size_t>(npg),
+                    stream))
     return MSGL_ERR_HIP;
   for (int32_t id : ids)
     if (id < 0 || id >= pool->num_pages) return MSGL_ERR_RANGE;
@@ -218,7 +223,8 @@ msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q
                           const int32_t* cu_extend_lens, int32_t batch,
                           int32_t total_extend_tokens, int32_t max_extend_len,
                           int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
-                          bool* nothing_to_do, int64_t* mtiles_out, int* waves_out) {
+                          bool* nothing_to_do, int64_t* mtiles_out, int* waves_out,
+                          hipStream_t stream) {
   *nothing_to_do = false;
   msgl_status st = check_pool(pool, layer);
   if (st != MSGL_OK) return st;
@@ -255,15 +261,16 @@ msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
     std::vector<int32_t> ti, pl, el, cu;
-    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(pl, prefix_lens, batch) ||
-        !copy_to_host(el, extend_lens, batch) || !copy_to_host(cu, cu_extend_lens, batch + 1))
+    if (!copy_to_host(ti, table_idx, batch, stream) || !copy_to_host(pl, prefix_lens, batch, stream) ||
+        !copy_to_host(el, extend_lens, batch, stream) ||
+        !copy_to_host(cu, cu_extend_lens, batch + 1, stream))
       return MSGL_ERR_HIP;
     if (cu[0] != 0 || cu[batch] != total_extend_tokens) return MSGL_ERR_RANGE;
     for (int32_t b = 0; b < batch; ++b) {
       if (pl[b] < 0 || el[b] < 0 || el[b] > max_extend_len ||
           static_cast<int64_t>(pl[b]) + el[b] > max_seq_len || cu[b + 1] - cu[b] != el[b])
         return MSGL_ERR_RANGE;
-      st = check_row_pages(page_table, page_table_stride, ti[b], pl[b] + el[b], pool);
+      st = check_row_pages(page_table, page_table_stride, ti[b], pl[b] + el[b], pool, stream);
       if (st != MSGL_OK) return st;
     }
   }
@@ -326,7 +333,8 @@ msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
     std::vector<int32_t> loc;
-    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens))) return MSGL_ERR_HIP;
+    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens), static_cast<hipStream_t>(stream)))
+      return MSGL_ERR_HIP;
     std::vector<int32_t> live;
     for (int32_t s : loc) {
       if (s >= num_slots(pool)) return MSGL_ERR_RANGE;
@@ -401,11 +409,12 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
     std::vector<int32_t> ti, sl;
-    if (!copy_to_host(ti, table_idx, batch) || !copy_to_host(sl, seq_lens, batch))
+    const hipStream_t cs = static_cast<hipStream_t>(stream);
+    if (!copy_to_host(ti, table_idx, batch, cs) || !copy_to_host(sl, seq_lens, batch, cs))
       return MSGL_ERR_HIP;
     for (int32_t b = 0; b < batch; ++b) {
       if (sl[b] < 0 || sl[b] > max_seq_len) return MSGL_ERR_RANGE;
-      st = check_row_pages(page_table, page_table_stride, ti[b], sl[b], pool);
+      st = check_row_pages(page_table, page_table_stride, ti[b], sl[b], pool, cs);
       if (st != MSGL_OK) return st;
     }
   }
@@ -429,7 +438,8 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
   msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                  table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
                                  total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
-                                 sm_scale, &nothing, &mtiles, &waves);
+                                 sm_scale, &nothing, &mtiles, &waves,
+                                 static_cast<hipStream_t>(stream));
   if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;
   const ExtendParams p = extend_params(pool, layer, q, q_row_stride, out, page_table,
@@ -453,7 +463,8 @@ msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void
   msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                  table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
                                  total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
-                                 sm_scale, &nothing, &mtiles, &waves);
+                                 sm_scale, &nothing, &mtiles, &waves,
+                                 static_cast<hipStream_t>(stream));
   if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;
   const size_t need =
@@ -494,7 +505,8 @@ msgl_status msgl_debug_gather_kv(const msgl_kv_pool* pool, int32_t layer,
   st = check_device();
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
-    st = check_row_pages(page_table, page_table_stride, row, len, pool);
+    st = check_row_pages(page_table, page_table_stride, row, len, pool,
+                         static_cast<hipStream_t>(stream));
     if (st != MSGL_OK) return st;
   }
   GatherParams p;
@@ -537,8 +549,9 @@ msgl_status msgl_rope_store_kv(const msgl_kv_pool* pool, int32_t layer, void* q,
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
     std::vector<int32_t> loc, pos;
-    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens)) ||
-        !copy_to_host(pos, positions, static_cast<size_t>(num_tokens)))
+    const hipStream_t cs = static_cast<hipStream_t>(stream);
+    if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens), cs) ||
+        !copy_to_host(pos, positions, static_cast<size_t>(num_tokens), cs))
       return MSGL_ERR_HIP;
     std::vector<uint8_t> seen(static_cast<size_t>(num_slots(pool)), 0);
     for (int32_t i = 0; i < num_tokens; ++i) {

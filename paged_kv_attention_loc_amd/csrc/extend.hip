@@ -40,10 +40,18 @@
 //     the S^T accumulator registers hold the keys -- so P^T feeds the
 //     second MFMA straight from registers.  Per-lane read addresses are
 //     computed once; the tile, stage and block parts are immediates;
-//   * q is scaled by scale*log2(e) and rounded to bf16 once per workgroup,
-//     and a ninth k-step per 32-key block (a constant ones operand against
-//     -m as a bf16 pair) subtracts the running maximum inside the MFMA, so
-//     a probability is one v_exp_f32 of the accumulator;
+//   * the MFMA takes q exactly as stored (bf16 in, fp32 accumulate): the
+//     scale*log2(e) factor is applied to the fp32 scores, fused with the
+//     subtraction of the running maximum, so a probability is one fma and
+//     one v_exp_f32 of the accumulator;
+//   * P.V runs on the fp16 MFMA (v_mfma_f32_32x32x16_f16): probabilities
+//     are rounded to fp16 (11 significant bits, against bf16's 8), and each
+//     wave turns the V rows it loaded into fp16 in place, right after its
+//     own DMA has landed and before the tile's barrier.  bf16 -> fp16 is
+//     exact for |V| in [2^-14, 65504]; below, V is rounded on fp16's
+//     subnormal grid (absolute error under 2^-25).  With bf16
+//     probabilities, peaked softmaxes (logits of tens) leave a few outputs
+//     per million beyond 1e-2 of exact attention; with fp16 none;
 //   * the running maximum only moves when a row's new maximum exceeds it by
 //     more than 2^8 in exp2 terms, so the O rescale is rare; masking runs
 //     only on tiles that cross a row's causal limit.
@@ -78,6 +86,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t extend_rsrc(const void* base, 
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// (lo, hi) rounded to nearest-even fp16 and packed (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+// a pair of bf16 values (one 32-bit word) as a pair of fp16 values
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+}
+// a.lo*b.lo + a.hi*b.hi + c on fp16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
 
 // Rows of the running maximum move only by more than this (log2 domain):
 // probabilities stay below 2^8, far inside bf16 / fp32 range.
@@ -160,16 +185,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   const int cu_r = p.cu_extend[r];
   const uint16_t* qp = p.q + static_cast<int64_t>(cu_r + ti) * p.q_stride +
                        static_cast<int64_t>(g * G + hh) * D + hi * 8;
-  // q is scaled by scale*log2(e) and rounded once to bf16, so that the
-  // scores leave the MFMA in log2 units, ready for exp2
+  // q enters the MFMA as stored; the scores are scaled in fp32
   bf16x8_t qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * p.scale_log2);
-    qop[ks] = x;
-  }
+  for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+  const float c2 = p.scale_log2;
 
   const int wrow0 = min(m0 + w * 32, M - 1);
   const int wrow1 = min(m0 + w * 32 + 31, M - 1);
@@ -222,26 +242,31 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
-  // m_run: the running maximum of the (log2-unit) scores of this lane's
-  // query column, kept exactly equal to a bf16 pair sum hi + lo.  A ninth
-  // k-step of S^T = K Q^T adds -m_run to every score: its A operand holds
-  // ones in k slots 0 and 1 (lanes of the first half, zeros elsewhere) and
-  // its B operand -hi and -lo in the same slots, so the softmax needs no
-  // per-score subtraction.  Before the first tile the offset is zero.
+  // m_run: the running maximum of the scaled scores s*scale*log2(e) of
+  // this lane's query column (log2 units)
   float m_run = -INFINITY;
   float l_run = 0.f;
-  bf16x8_t a_ones, b_negm;
+
+  // the V rows this wave loaded into `stage`, bf16 -> fp16 in place (its
+  // IPW KiB of the V tile; the DMA's LDS writes are waited for first)
+  auto convert_v = [&](int stage) {
+    uint8_t* vb = lds + stage * STAGE + K_BYTES + w * IPW * 1024 + lane * 16;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a_ones[e] = static_cast<__bf16>((hi == 0 && e < 2) ? 1.f : 0.f);
-    b_negm[e] = static_cast<__bf16>(0.f);
-  }
+    for (int k = 0; k < IPW; ++k) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(vb + k * 1024);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+      *reinterpret_cast<u32x4_t*>(vb + k * 1024) = x;
+    }
+  };
 
   // prologue: tile 0 in stage 0; tile 1 on its way to stage 1; tile 2's
   // entries in flight (the barrier's fence waits for the DMA)
   fetch_entries(0);
   issue_dma(0, 0);
   if (ntiles > 1) fetch_entries(1);
+  convert_v(0);
   __syncthreads();
   if (ntiles > 1) issue_dma(1, 1);
   if (ntiles > 2) fetch_entries(2);
@@ -290,34 +315,30 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
       bf16x8_t ka[KS];
-      bf16x8_t va[4];
+      f16x8_t va[4];
       auto load_va = [&](int cb, int kk) {
         const i16x4_t lo = lds_read_tr16(vt + vofs[cb] + kk * 16 * ROWB);
         const i16x4_t hi8 = lds_read_tr16(vt + vofs[cb] + (kk * 16 + 8) * ROWB);
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(f16x8_t, __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7));
       };
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks]);
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ones, b_negm, sc[0], 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[0], 0, 0, 0);
         ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + kofs[ks] + 32 * ROWB);
       }
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ones, b_negm, sc[1], 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qop[ks], sc[1], 0, 0, 0);
         if (ks < 4) va[ks] = load_va(0, ks);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -332,19 +353,19 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
           for (int e = 0; e < 16; ++e)
             if (32 * kb + 8 * (e >> 2) + (e & 3) > lim_rel) sc[kb][e] = -INFINITY;
       }
-      // ---- online softmax in the log2 domain.  The scores already are
-      // s - m_off (m_off: m_run, or 0 before the first tile).  Fast path:
-      // exponentiate them as they stand; that is exact softmax arithmetic as
-      // long as no probability exceeds 2^8, which a lane row sum of at most
-      // 2^8 guarantees.  Otherwise (and on a wave's first tile, whose
-      // maximum is still -inf) the tile maximum is taken, the running
-      // maximum moves if the tile's exceeds it by more than 2^8, and the
-      // probabilities are recomputed against the new maximum.
+      // ---- online softmax in the log2 domain, on x = s*scale*log2(e).
+      // Fast path: exponentiate against the running maximum as it stands;
+      // that is exact softmax arithmetic as long as no probability exceeds
+      // 2^8, which a lane row sum of at most 2^8 guarantees.  Otherwise (and
+      // on a wave's first tile, whose maximum is still -inf) the tile
+      // maximum is taken, the running maximum moves if the tile's exceeds
+      // it by more than 2^8, and the probabilities are recomputed against
+      // the new maximum.
       float lsum = 0.f;
-      bf16x8_t pop[4];
-      constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
-      auto probabilities = [&](float delta) {  // p = 2^(score - delta)
-        // the row sum adds the bf16 values that the P.V product uses, in
+      f16x8_t pop[4];
+      constexpr uint32_t kOnes = 0x3C003C00u;  // fp16 (1, 1)
+      auto probabilities = [&](float mref) {  // p = 2^(s*c2 - mref)
+        // the row sum adds the fp16 values that the P.V product uses, in
         // four independent partial sums (one per k-step) so that the dot2
         // accumulations do not form one serial chain
         float part[4];
@@ -355,47 +376,32 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             const int e = 8 * (kk & 1) + 2 * e2;
-            const float p0 = fast_exp2(sc[kk >> 1][e] - delta);
-            const float p1 = fast_exp2(sc[kk >> 1][e + 1] - delta);
-            wds[e2] = pack_bf16(p0, p1);
-            part[kk] = dot2_bf16(wds[e2], kOnes, part[kk]);
+            const float p0 = fast_exp2(__builtin_fmaf(sc[kk >> 1][e], c2, -mref));
+            const float p1 = fast_exp2(__builtin_fmaf(sc[kk >> 1][e + 1], c2, -mref));
+            wds[e2] = pack_f16(p0, p1);
+            part[kk] = dot2_f16(wds[e2], kOnes, part[kk]);
           }
-          pop[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
+          pop[kk] = __builtin_bit_cast(f16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
         }
         lsum = (part[0] + part[1]) + (part[2] + part[3]);
       };
       bool slow = m_run == -INFINITY;
       if (__builtin_amdgcn_ballot_w64(slow) == 0) {
-        probabilities(0.f);
+        probabilities(m_run);
         slow = !(lsum <= kSumLimit);  // also catches inf
       }
       if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-        const float m_off = m_run == -INFINITY ? 0.f : m_run;
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-        mx = xor32_max(mx) + m_off;
+        mx = xor32_max(mx) * c2;  // scale > 0: the maximum commutes with it
         const bool move = mx > m_run + kMaxSlack;
-        // a new maximum is rounded to a bf16 pair sum, which the offset
-        // k-step then subtracts exactly
-        float mnew = m_run;
-        __bf16 mh = static_cast<__bf16>(0.f), ml = static_cast<__bf16>(0.f);
-        if (move) {
-          mh = static_cast<__bf16>(mx);
-          ml = static_cast<__bf16>(mx - static_cast<float>(mh));
-          mnew = static_cast<float>(mh) + static_cast<float>(ml);
-        }
+        const float mnew = move ? mx : m_run;
         const float alpha = fast_exp2(m_run - mnew);
-        probabilities(mnew - m_off);
-        if (move) {
-          m_run = mnew;
-          if (hi == 0) {
-            b_negm[0] = -mh;
-            b_negm[1] = -ml;
-          }
-        }
+        probabilities(mnew);
+        m_run = mnew;
         // the rescale is skipped when no row of the wave moved its maximum
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
           l_run *= alpha;
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], pop[kk], o[cb], 0, 0, 0);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kk], pop[kk], o[cb], 0, 0, 0);
           if (cb + 1 < CB) va[kk] = load_va(cb + 1, kk);
         }
       }
@@ -424,9 +430,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     // every wave is done with this stage and tile t+1 has landed in the
-    // other one (vmcnt(0): the DMA is a vector-memory operation); then
-    // tile t+2 goes into this stage and tile t+3's page entries go out
+    // other one (vmcnt(0): the DMA is a vector-memory operation), its V
+    // rows turned to fp16 by the waves that loaded them; then tile t+2
+    // goes into this stage and tile t+3's page entries go out
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (t + 1 < ntiles) convert_v(ST ^ 1);
     __syncthreads();
     if (t + 2 < ntiles) issue_dma(t + 2, ST);
     if (t + 3 < ntiles) fetch_entries(t + 3);

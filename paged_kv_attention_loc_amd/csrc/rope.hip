@@ -2,8 +2,8 @@
 // builder.
 //
 // The pages list rotary position embeddings among the model layers ("Code
-// Notes: mini-sglang", section "Layers", get_rope / set_rope_device; model
-// configuration, RotaryConfig) without the formula.  The standard rotary
+// Structure", section Model Layers, get_rope / set_rope_device; section
+// Model Definitions, RotaryConfig) without the formula.  The standard rotary
 // embedding is used, with the half-split pairing of the Llama family: for
 // i < d/2 the pair (x_i, x_{i+d/2}) at position p turns by the angle
 // a = p * base^(-2i/d):
