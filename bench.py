@@ -124,9 +124,9 @@ class Prepared:
         self.max_ext = int(ph.extend_lens.max())
         self.out = torch.empty_like(self.q)
         import paged_kv_attention_loc_amd as msgl
-        need = msgl.paged_decode_workspace_size(ph.batch, wl.num_qo_heads, wl.num_kv_heads,
-                                                wl.head_dim, self.max_len)
-        self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        need = msgl.paged_decode_workspace_size(ph.batch, wl.num_qo_heads, wl.head_dim,
+                                                self.max_len, wl.page_size)
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
 
 def run_store(msgl, p):
@@ -286,7 +286,7 @@ def mixed_stats(msgl, dev, iters=10):
     el_ext = i32(ph.extend_lens[ext], dev)
     out = torch.empty_like(p.q)
     out_dec, out_ext = torch.empty_like(q_dec), torch.empty_like(q_ext)
-    ws_dec = torch.empty(max(msgl.paged_decode_workspace_size(64, 32, 8, 128, p.max_len), 16),
+    ws_dec = torch.zeros(max(msgl.paged_decode_workspace_size(64, 32, 128, p.max_len, 16), 256),
                          dtype=torch.uint8, device=dev)
 
     def mixed():

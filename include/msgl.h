@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MSGL_ABI_VERSION 1
+#define MSGL_ABI_VERSION 2
 
 typedef int32_t msgl_status;
 #define MSGL_OK 0
@@ -103,16 +103,18 @@ msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k
                           const int32_t* out_loc, int32_t num_tokens, void* stream);
 
 /*
- * Bytes of workspace msgl_paged_decode needs for a batch with these sizes
- * (fp32 split-KV partial outputs and their softmax statistics); 0 when no
- * request can need more than one split.  The value
- * depends only on the arguments (and on MSGL_DECODE_SPLIT if set), so a
- * workspace sized once for the largest batch and max_seq_len serves every
- * smaller call.  Returns 0 for invalid sizes.
+ * Bytes of workspace msgl_paged_decode needs for a batch with these sizes:
+ * a map of each request's pieces, and the fp32 partial outputs, with their
+ * softmax statistics, of requests split over several workgroups.  It
+ * depends on batch, num_qo_heads, head_dim and max_seq_len only (page_size
+ * is accepted and checked, >= 1, but does not change the layout: the
+ * decode splits tokens, not pages), and it grows with batch and
+ * max_seq_len, so a workspace sized once for the largest batch and
+ * max_seq_len serves every smaller call.  Returns 0 for batch 0 and for
+ * invalid sizes.
  */
-size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
-                                        int32_t num_kv_heads, int32_t head_dim,
-                                        int32_t max_seq_len);
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+                                        int32_t max_seq_len, int32_t page_size);
 
 /*
  * paged_decode: one query token per request attends to all seq_lens[r]
@@ -129,15 +131,18 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
  *                 valid page ids (entries past that are never read).
  *   table_idx   : (batch,) int32 row indices.
  *   seq_lens    : (batch,) int32 in [0, max_seq_len]; 0 marks a padding row.
- *   max_seq_len : host-side bound used to size the grid and the workspace.
+ *   max_seq_len : host-side bound used to size the grid and the workspace
+ *                 (at most 2048 * 4096 tokens).
  *   sm_scale    : softmax scale, normally 1/sqrt(head_dim).
- *   workspace   : device buffer of >= msgl_paged_decode_workspace_size(...)
- *                 bytes; its contents need no initialisation.  Calls that
- *                 share a workspace must not overlap in time (same stream,
- *                 or synchronised).
- * Long sequences are split into KV chunks processed in parallel; a second
- * kernel on the same stream merges the partial results with a log-sum-exp
- * combine.
+ *   workspace   : device buffer, 256-byte aligned, of >=
+ *                 msgl_paged_decode_workspace_size(batch, num_qo_heads,
+ *                 head_dim, max_seq_len, page_size) bytes; its contents
+ *                 need no initialisation.  Calls that share a workspace must
+ *                 not overlap in time (same stream, or synchronised).
+ * The batch's tokens are split evenly over the workgroups, so a long
+ * sequence is processed by several of them in parallel; a second kernel on
+ * the same stream merges the partial results with a log-sum-exp combine.
+ * Batches above 2048 requests are processed 2048 at a time.
  */
 msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const void* q,
                               int64_t q_row_stride, void* out, const int32_t* page_table,
@@ -295,17 +300,16 @@ msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph);
  * BaseAttnBackend row -- HybridBackend keeps a prefill and a decode
  * backend; Scheduler Layer table, PrefillManager row -- chunked prefill).
  * Arguments as for paged_extend, plus the decode workspace:
- * msgl_paged_decode_workspace_size(batch, num_qo_heads, num_kv_heads,
- * head_dim, max_seq_len) bytes.  Rows are dispatched on the device by
+ * msgl_paged_decode_workspace_size(batch, num_qo_heads, head_dim,
+ * max_seq_len, page_size) bytes.  Rows are dispatched on the device by
  * extend_lens, so the host never needs the lengths:
- *   - a row with extend_lens[r] == 1 is a decode row: split-KV decode and
- *     merge, with q / out row cu_extend_lens[r] and length
- *     prefix_lens[r] + 1;
+ *   - a row with extend_lens[r] == 1 is a decode row: decode and merge,
+ *     with q / out row cu_extend_lens[r] and length prefix_lens[r] + 1;
  *   - every other row goes through the extend kernel (rows with
  *     extend_lens[r] == 0 produce nothing).
  * The result equals paged_extend on the same batch within the attention
  * tolerance; the decode rows equal paged_decode on those rows exactly.
- * Three launches on `stream` (split decode, merge, extend); calls sharing a
+ * Three launches on `stream` (decode, merge, extend); calls sharing a
  * workspace must not overlap.
  */
 msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void* q,

@@ -35,6 +35,7 @@ __all__ = [
     "store_kv",
     "paged_decode",
     "paged_decode_workspace_size",
+    "decode_workspace",
     "paged_extend",
     "debug_gather_kv",
     "DecodeGraph",
@@ -177,11 +178,22 @@ def msgl_store_kv(pool: torch.Tensor, layer: int, k: torch.Tensor, v: torch.Tens
     _check(st, "msgl_store_kv")
 
 
-def msgl_paged_decode_workspace_size(batch: int, num_qo_heads: int, num_kv_heads: int,
-                                     head_dim: int, max_seq_len: int) -> int:
-    """Bytes of decode workspace (fp32 split partials); 0 if none is needed."""
-    return int(load_library().msgl_paged_decode_workspace_size(batch, num_qo_heads, num_kv_heads,
-                                                               head_dim, max_seq_len))
+def msgl_paged_decode_workspace_size(batch: int, num_qo_heads: int, head_dim: int,
+                                     max_seq_len: int, page_size: int) -> int:
+    """Bytes of decode workspace (piece map and fp32 partials of split
+    requests); 0 for an empty batch.  Contents need no initialisation."""
+    return int(load_library().msgl_paged_decode_workspace_size(batch, num_qo_heads, head_dim,
+                                                               max_seq_len, page_size))
+
+
+def decode_workspace(batch: int, num_qo_heads: int, head_dim: int, max_seq_len: int,
+                     page_size: int, device="cuda") -> Optional[torch.Tensor]:
+    """A zeroed decode workspace for calls up to these sizes (None if no
+    call of that size needs one)."""
+    need = msgl_paged_decode_workspace_size(batch, num_qo_heads, head_dim, max_seq_len, page_size)
+    if need == 0:
+        return None
+    return torch.zeros(need, dtype=torch.uint8, device=device)
 
 
 def msgl_paged_decode(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
@@ -199,9 +211,8 @@ def msgl_paged_decode(pool: torch.Tensor, layer: int, q: torch.Tensor, page_tabl
         raise ValueError("out must be a contiguous bf16 tensor shaped like q")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    need = msgl_paged_decode_workspace_size(B, hq, ps.num_kv_heads, d, max_seq_len)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, hq, d, max_seq_len, ps.page_size, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if page_table.dim() != 2:
@@ -258,9 +269,8 @@ def msgl_paged_mixed(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table
         raise ValueError("out must be a contiguous bf16 tensor shaped like q")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    need = msgl_paged_decode_workspace_size(B, hq, ps.num_kv_heads, d, max_seq_len)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, hq, d, max_seq_len, ps.page_size, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if page_table.dim() != 2:
@@ -377,8 +387,8 @@ class DecodeGraph:
         self.out_loc = torch.full((batch,), -1, dtype=torch.int32, device=dev)
         self.table_idx = torch.zeros((batch,), dtype=torch.int32, device=dev)
         self.seq_lens = torch.zeros((batch,), dtype=torch.int32, device=dev)
-        need = msgl_paged_decode_workspace_size(batch, num_qo_heads, hkv, d, max_seq_len)
-        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        need = msgl_paged_decode_workspace_size(batch, num_qo_heads, d, max_seq_len, ps.page_size)
+        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(d)
         self._pool_struct = ps

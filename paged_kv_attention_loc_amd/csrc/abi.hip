@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/msgl.h: argument validation
 // (before any HIP call), the gfx950 check, the optional checked mode, and
 // the launch of the kernels on the caller's stream.
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -82,11 +83,6 @@ msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_he
   return MSGL_OK;
 }
 
-// Decode workspace layout: fp32 partial outputs (batch, max_chunks, Hq, d),
-// then their (max, sum) pairs, 256-byte aligned.  The split size (see
-// decode_chunk) is doubled until no request needs more than
-// kMaxDecodeSplits splits.
-constexpr int64_t kMaxDecodeSplits = 4096;
 // Waves per extend workgroup (32 query rows each): 8 by default;
 // MSGL_EXTEND_WAVES=4 selects 128-row workgroups.
 int extend_waves() {
@@ -94,23 +90,45 @@ int extend_waves() {
   return (v && std::atoi(v) == 4) ? 4 : 8;
 }
 
-// Tokens per decode split (a multiple of 64): 384 by default.  Measured
-// over 128-512 with nontemporal K/V loads, 256-384 tie on the Llama-3-8B
-// geometry batch and 384 is ~3% faster on the Qwen3-30B-A3B one (long,
-// lognormal lengths: fewer partials).  MSGL_DECODE_SPLIT overrides it.
-int32_t decode_chunk(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t max_seq_len) {
-  int64_t c = 384;
-  const char* v = std::getenv("MSGL_DECODE_SPLIT");
-  if (v && v[0]) {
-    const long e = std::strtol(v, nullptr, 10);
-    if (e >= 64 && e <= (1 << 20)) c = (e + 63) / 64 * 64;
-  }
-  while ((static_cast<int64_t>(max_seq_len) + c - 1) / c > kMaxDecodeSplits) c *= 2;
-  return static_cast<int32_t>(c);
+// kv heads per decode workgroup: the largest power of two <= 8 dividing Hkv
+int32_t decode_head_group(int32_t num_kv_heads) {
+  int32_t hg = 8;
+  while (num_kv_heads % hg) hg >>= 1;
+  return hg;
 }
 
-// Checked mode reads device metadata on the caller's stream, after the work
-// already queued there (which may be what wrote it), and waits for it.
+// Decode workspace (bytes, each part 256-byte aligned): a piece map, one
+// int2 per request; then, for each launch of up to kDecodeBatch requests,
+// the fp32 partial outputs of its pieces (pieces, Hq, d) and their
+// (max, sum) pairs.  A launch of b
+// requests splits at most b * max_seq_len tokens over at most kDecodeGrid
+// ranges of >= kDecodeMinTokens, and piece i + r of range i and request r
+// is below ranges + b.
+int64_t decode_pieces(int64_t b, int64_t max_seq_len) {
+  const int64_t ranges = std::min<int64_t>(kDecodeGrid, (b * max_seq_len + kDecodeMinTokens - 1) / kDecodeMinTokens);
+  return ranges + b;
+}
+struct DecodeWorkspace {
+  int64_t map_bytes, o_bytes, ml_bytes;
+};
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+DecodeWorkspace decode_workspace(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+                                 int32_t max_seq_len) {
+  DecodeWorkspace w{0, 0, 0};
+  if (batch <= 0) return w;
+  int64_t pieces = 0;
+  for (int64_t b0 = 0; b0 < batch; b0 += kDecodeBatch)
+    pieces += decode_pieces(std::min<int64_t>(kDecodeBatch, batch - b0), max_seq_len);
+  w.map_bytes = align256(static_cast<int64_t>(batch) * 8);
+  w.o_bytes = align256(pieces * num_qo_heads * head_dim * 4);
+  w.ml_bytes = pieces * num_qo_heads * 2 * 4;
+  return w;
+}
+
+// Longest sequence a decode call takes: the token total of a launch fits
+// in int32.
+constexpr int64_t kDecodeMaxSeqLen = (int64_t{1} << 31) / kDecodeBatch - 1;
+
 template <typename T>
 bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
   dst.resize(n);
@@ -135,14 +153,14 @@ msgl_status check_row_pages(const int32_t* page_table, int64_t stride, int32_t r
   return MSGL_OK;
 }
 
-// Kernel parameters of a decode over validated arguments (workspace NULL
-// when no request needs more than one split).
+// Kernel parameters of a decode over validated arguments.
 DecodeParams decode_params(const msgl_kv_pool* pool, int32_t layer, const void* q,
                            int64_t q_row_stride, void* out, const int32_t* page_table,
                            int32_t page_table_stride, const int32_t* table_idx,
                            const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
                            int32_t max_seq_len, float sm_scale, void* workspace) {
   const int32_t d = pool->head_dim;
+  const DecodeWorkspace ws = decode_workspace(batch, num_qo_heads, d, max_seq_len);
   DecodeParams p;
   p.k_cache = k_half(pool, layer);
   p.v_cache = v_half(pool, layer);
@@ -153,30 +171,52 @@ DecodeParams decode_params(const msgl_kv_pool* pool, int32_t layer, const void* 
   p.pt_stride = page_table_stride;
   p.table_idx = table_idx;
   p.seq_lens = seq_lens;
+  p.batch = batch;
   p.num_kv_heads = pool->num_kv_heads;
   p.group = num_qo_heads / pool->num_kv_heads;
+  p.head_group = decode_head_group(pool->num_kv_heads);
   p.page_size = pool->page_size;
-  p.chunk = decode_chunk(batch, pool->num_kv_heads, max_seq_len);
-  p.max_chunks = static_cast<int32_t>((static_cast<int64_t>(max_seq_len) + p.chunk - 1) / p.chunk);
-  if (p.max_chunks < 1) p.max_chunks = 1;
+  p.stages = 2;
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
-  p.page_shift = page_shift_of(pool->page_size);
   p.max_seq_len = max_seq_len;
   p.scale_log2 = sm_scale * kLog2e;
   p.mixed_prefix = nullptr;
   p.mixed_extend = nullptr;
   p.mixed_cu = nullptr;
-  if (workspace) {
-    const int64_t units = static_cast<int64_t>(batch) * p.max_chunks * (num_qo_heads + 1);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(ws);
-    p.ws_ml = reinterpret_cast<float*>(ws + ((units * d * 4 + 255) / 256) * 256);
-  } else {
-    p.ws_o = nullptr;
-    p.ws_ml = nullptr;
-  }
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.ws_map = reinterpret_cast<int2*>(base);
+  p.ws_o = reinterpret_cast<float*>(base + ws.map_bytes);
+  p.ws_ml = reinterpret_cast<float*>(base + ws.map_bytes + ws.o_bytes);
   return p;
+}
+
+// One launch per kDecodeBatch requests, each with its own piece region of
+// the workspace.
+hipError_t launch_decode_batches(const DecodeParams& p, int32_t head_dim, hipStream_t stream) {
+  const int64_t Hq = static_cast<int64_t>(p.num_kv_heads) * p.group;
+  int64_t piece_off = 0;
+  for (int32_t b0 = 0; b0 < p.batch; b0 += kDecodeBatch) {
+    DecodeParams s = p;
+    s.batch = std::min<int32_t>(kDecodeBatch, p.batch - b0);
+    s.table_idx += b0;
+    if (p.mixed_cu) {
+      s.mixed_prefix += b0;
+      s.mixed_extend += b0;
+      s.mixed_cu += b0;
+    } else {
+      s.seq_lens += b0;
+      s.q += b0 * p.q_stride;
+      s.out += static_cast<int64_t>(b0) * Hq * head_dim;
+    }
+    s.ws_map += b0;
+    s.ws_o += piece_off * Hq * head_dim;
+    s.ws_ml += piece_off * Hq * 2;
+    piece_off += decode_pieces(s.batch, p.max_seq_len);
+    const hipError_t e = launch_decode(s, head_dim, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Kernel parameters of an extend over validated arguments.
@@ -362,19 +402,12 @@ msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k
   return hip_status(launch_store_kv(p, vec, static_cast<hipStream_t>(stream)));
 }
 
-size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
-                                        int32_t num_kv_heads, int32_t head_dim,
-                                        int32_t max_seq_len) {
-  if (batch < 0 || num_qo_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 0)
-    return 0;
-  const int32_t chunk = decode_chunk(batch, num_kv_heads, max_seq_len);
-  const int64_t mc = (static_cast<int64_t>(max_seq_len) + chunk - 1) / chunk;
-  if (mc <= 1) return 0;
-  // one unit of padding per (request, chunk) row: see decode_split_kernel
-  const int64_t units = static_cast<int64_t>(batch) * mc * (num_qo_heads + 1);
-  const int64_t o_bytes = units * head_dim * 4;
-  const int64_t ml_bytes = units * 2 * 4;
-  return static_cast<size_t>(((o_bytes + 255) / 256) * 256 + ml_bytes);
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+                                        int32_t max_seq_len, int32_t page_size) {
+  // page_size does not change the layout: ranges split tokens, not pages
+  if (batch < 0 || num_qo_heads < 1 || head_dim < 1 || max_seq_len < 0 || page_size < 1) return 0;
+  const DecodeWorkspace w = decode_workspace(batch, num_qo_heads, head_dim, max_seq_len);
+  return static_cast<size_t>(w.map_bytes + w.o_bytes + w.ml_bytes);
 }
 
 msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const void* q,
@@ -401,10 +434,11 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   if (page_table_stride < 1) return MSGL_ERR_SHAPE;
   const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
   if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
+  if (max_seq_len > kDecodeMaxSeqLen) return MSGL_ERR_UNSUPPORTED;
   const size_t need =
-      msgl_paged_decode_workspace_size(batch, num_qo_heads, pool->num_kv_heads, d, max_seq_len);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return MSGL_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return MSGL_ERR_SHAPE;
+      msgl_paged_decode_workspace_size(batch, num_qo_heads, d, max_seq_len, pool->page_size);
+  if (!workspace || workspace_bytes < need) return MSGL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MSGL_ERR_SHAPE;
   st = check_device();
   if (st != MSGL_OK) return st;
   if (env_on("MSGL_CHECK")) {
@@ -420,8 +454,8 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
   }
   const DecodeParams p = decode_params(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                        table_idx, seq_lens, batch, num_qo_heads, max_seq_len,
-                                       sm_scale, need > 0 ? workspace : nullptr);
-  return hip_status(launch_decode(p, d, batch, static_cast<hipStream_t>(stream)));
+                                       sm_scale, workspace);
+  return hip_status(launch_decode_batches(p, d, static_cast<hipStream_t>(stream)));
 }
 
 msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const void* q,
@@ -467,19 +501,20 @@ msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void
                                  static_cast<hipStream_t>(stream));
   if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;
+  if (max_seq_len > kDecodeMaxSeqLen) return MSGL_ERR_UNSUPPORTED;
   const size_t need =
-      msgl_paged_decode_workspace_size(batch, num_qo_heads, pool->num_kv_heads, d, max_seq_len);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return MSGL_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return MSGL_ERR_SHAPE;
+      msgl_paged_decode_workspace_size(batch, num_qo_heads, d, max_seq_len, pool->page_size);
+  if (!workspace || workspace_bytes < need) return MSGL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MSGL_ERR_SHAPE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // rows with one new token: split-KV decode and its merge
   DecodeParams pd = decode_params(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                   table_idx, nullptr, batch, num_qo_heads, max_seq_len, sm_scale,
-                                  need > 0 ? workspace : nullptr);
+                                  workspace);
   pd.mixed_prefix = prefix_lens;
   pd.mixed_extend = extend_lens;
   pd.mixed_cu = cu_extend_lens;
-  st = hip_status(launch_decode(pd, d, batch, s));
+  st = hip_status(launch_decode_batches(pd, d, s));
   if (st != MSGL_OK) return st;
   // the other rows: causal extend
   const ExtendParams pe = extend_params(pool, layer, q, q_row_stride, out, page_table,

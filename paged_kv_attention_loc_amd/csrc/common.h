@@ -147,8 +147,17 @@ struct GatherParams {
   int32_t num_slots;
 };
 
+// Decode works on whole token rows and balanced token ranges: the batch's
+// tokens, requests laid end to end, are split evenly over kDecodeGrid
+// workgroups per group of `head_group` kv heads; a workgroup streams the
+// group's part of every K and V row of its range, request by request.
+constexpr int kDecodeGrid = 512;       // workgroups per head group and launch (two per CU)
+constexpr int kDecodeBatch = 2048;     // requests per launch (prefix sums in LDS)
+constexpr int kDecodeWindow = 1024;    // tokens whose slots are staged at once
+constexpr int kDecodeMinTokens = 64;   // tokens per workgroup at least
+
 struct DecodeParams {
-  const uint16_t* k_cache;
+  const uint16_t* k_cache;  // K half of the layer, (slots, Hkv, d)
   const uint16_t* v_cache;
   const uint16_t* q;
   int64_t q_stride;  // elements between consecutive requests' q rows
@@ -157,18 +166,23 @@ struct DecodeParams {
   int64_t pt_stride;
   const int32_t* table_idx;
   const int32_t* seq_lens;
-  float* ws_o;   // (batch, max_chunks, Hq, D) unnormalised partial outputs
-  float* ws_ml;  // (batch, max_chunks, Hq, 2) running max (log2 domain), sum
+  // workspace: per request, (first piece, pieces) of this call; the
+  // unnormalised partial outputs of the (workgroup i, request r) pieces, at
+  // piece i + r: (pieces, Hq, D); their (running maximum in log2 units, sum)
+  // pairs (pieces, Hq, 2)
+  int2* ws_map;
+  float* ws_o;
+  float* ws_ml;
+  int32_t batch;       // requests of this launch, <= kDecodeBatch
   int32_t num_kv_heads;
-  int32_t group;
+  int32_t group;       // q heads per kv head
+  int32_t head_group;  // kv heads per workgroup: a power of two <= 8 dividing num_kv_heads
   int32_t page_size;
-  int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
-  int32_t chunk;  // tokens per split, a multiple of 64
-  int32_t max_chunks;
+  int32_t stages;      // LDS stages of the K/V pipeline (2-4)
   int32_t max_seq_len;
   int32_t num_slots;
   uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
-  float scale_log2;  // sm_scale * log2(e)
+  float scale_log2;     // sm_scale * log2(e)
   // mixed batches (all three set, seq_lens unused): request r is a decode
   // row only when mixed_extend[r] == 1 -- the others belong to the extend
   // kernel and are skipped; its length is mixed_prefix[r] + 1 and its q /
@@ -242,7 +256,8 @@ struct AllocParams {
 // Launchers (defined next to their kernels); return the HIP status.
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStream_t stream);
+// one launch of at most kDecodeBatch requests
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
 // `waves` (4 or 8) sets the query rows per workgroup (32 per wave); the
 // caller sizes p.num_mtiles for it.
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,

@@ -1,331 +1,496 @@
-// Split-KV paged decode attention and the log-sum-exp merge of its partials.
+// Paged decode attention over whole token rows and balanced token ranges,
+// with the merge of split requests folded into the same launch.
 //
 // Decode attends one new query token per request over all of its KV, read
 // through the request's page_table row ("Code Notes: mini-sglang", Engine
 // Layer table rows BaseAttnBackend / GraphRunner; Scheduler Layer table row
-// TableManager).  The work is HBM-bound: every K/V byte is read once and
-// used for G = q_heads / kv_heads query heads, so the kernel is built to
-// keep many waves -- and so many loads -- in flight per CU, with no matrix
-// cores involved.
-//
-// One wave64 workgroup handles (request, kv head, chunk of `chunk` tokens)
-// in tiles of 32 tokens.  A wave needs about 9-11 KiB of LDS and few
-// registers, so a CU holds 16 of them and their loads overlap each other's
-// arithmetic; chunks are short (384 tokens by default) so that many
-// independent waves are in flight while the split partials stay a few
-// percent of the KV bytes.
-//   * the K/V loads carry the nontemporal hint: every byte is read once;
-//   * addressing: one vector load per tile fetches the tile's page ids
-//     (lane t: token t), one tile ahead; each token's row byte offset is
-//     then moved into an SGPR (v_readlane) and every K/V load is a buffer
-//     load of that whole token row (4 bytes per lane, one row per
-//     instruction).  No lane holds a 64-bit address, and an offset past
-//     the pool reads zeros instead of faulting;
-//   * q.K: two neighbouring lanes own one token (half of the channels
-//     each).  K rows pass through LDS with one 16-byte piece of padding per
-//     row (conflict-free reads, addresses base + immediate), q is broadcast
-//     from LDS one head at a time, v_dot2_f32_bf16 does the products and one
-//     DPP add joins the halves;
-//   * softmax statistics are kept per head in the log2 domain (scale folded
-//     into the exponent); the tile maximum comes from DPP row reductions;
-//   * p.V: each lane owns two channels of every token and keeps its V words
-//     in registers; two tokens' values are paired with v_perm and weighted
-//     by the matching bf16 pair of probabilities (an LDS broadcast) in one
-//     v_dot2_f32_bf16: two accumulators per head;
-//   * a request with a single chunk writes its bf16 output directly; longer
-//     ones write fp32 partials (unnormalised o, max, sum) that the merge
-//     kernel combines.
+// TableManager).  Every K/V byte is read once, so the kernel is built around
+// the HBM stream:
+//   * the batch's tokens, requests laid end to end, are split into equal
+//     ranges, one per workgroup (kDecodeGrid of them per group of kv heads):
+//     every workgroup moves the same number of bytes whatever the length
+//     mix, and no workgroup is launched for nothing.  Each workgroup takes
+//     the token prefix sums of the batch into LDS and walks the requests its
+//     range touches;
+//   * one workgroup of 8 waves streams the group's part of each token row --
+//     a token's row in the pool holds every kv head (BaseKVCachePool row of
+//     the same table: (..., kv_heads, head_dim) is innermost), so that part
+//     is one contiguous run of up to 2 KiB.  16 bytes a lane, 1 KiB of
+//     consecutive LDS per wave instruction (buffer_load ... lds), spread over
+//     all 8 waves, a tile ahead of the arithmetic.  The DMA is issued as
+//     assembly: the compiler would otherwise drain it before every LDS read,
+//     because it cannot tell which stage those reads touch;
+//   * tiles hold KB tokens (8 to 64: 16 KiB of K and 16 KiB of V), S stages,
+//     one barrier per tile; the slots of up to kDecodeWindow tokens are
+//     computed at a time into LDS;
+//   * wave w computes kv head w of the group on the matrix cores
+//     (v_mfma_f32_16x16x32_bf16): S^T = K Q^T with the G <= 16 query heads
+//     as the 16 columns, then O^T = V^T P^T.  Each lane holds 4 keys of one
+//     head per 16-key block, so the 32 k-slots of the P.V product carry 16
+//     keys twice: once with the bf16-rounded probability and once with the
+//     bf16 remainder p - bf16(p), against the same V (one ds_read_b64_tr_b16
+//     transpose read used twice).  The product thus weights V with ~16-bit
+//     probabilities in one MFMA, and V enters exactly as stored;
+//   * the online softmax is in the log2 domain on fp32 scores (scale folded
+//     into one fma); the running maximum moves only when a score exceeds it
+//     by more than 2^8, so the rescale of O is rare;
+//   * a request inside one range writes its bf16 output directly.  A
+//     request spread over several ranges writes one fp32 partial per range
+//     (piece i + r of range i and request r: both indices only grow along
+//     the token axis, so pieces never collide), and a second kernel merges
+//     them with a log-sum-exp combine, one wave per (request, q head).
+//     Merging inside the first kernel -- the last range of a request to
+//     finish, found with an atomic counter -- measured ~25 us slower on the
+//     Llama-3-8B-geometry batch: the agent-scope release that publishes the
+//     partials writes back the whole L2 of an XCD, once per range.
+#include <type_traits>
+
 #include "common.h"
 
 namespace msgl {
 
 namespace {
 
-template <int D>
-struct DecodeShape {
-  static constexpr int TILE = 32;     // tokens per tile
-  static constexpr int LPT = D / 8;   // 16-byte pieces per token row
-  static constexpr int HPC = LPT / 2; // pieces per q.K half-row
-  static constexpr int CPL = D / 2;   // 4-byte words per token row
-  // LDS row pitch of K in words: one 16-byte piece of padding per row
-  static constexpr int KROW = CPL + 4;
-};
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Waves per SIMD the register allocation must leave room for: occupancy is
-// what hides the HBM latency here.
-template <int GM>
-struct DecodeOccupancy {
-  static constexpr int value = GM <= 8 ? 4 : 2;
-};
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageBytes = 32768;  // K tile then V tile
+// Rows of the running maximum move only by more than this (log2 domain).
+constexpr float kMaxSlack = 8.f;
+// A lane's sum of 4 probabilities above this means one may exceed 2^kMaxSlack.
+constexpr float kSumLimit = 256.f;
 
-// Cache policy of the K/V loads: nontemporal (the nt bit of the buffer
-// load).  Each K/V byte is read exactly once per launch, so the stream is
-// marked as such and does not displace what the caches hold for the
-// kernels around it; measured, the decode itself also runs faster so.
-constexpr int kStream = 2;
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(__attribute__((address_space(3))) const uint8_t*)(addr));
+}
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  // dword 3 = 0x00020000: 32-bit data format, raw (unswizzled) addressing
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+// buffer resource words: base, 32-bit range, raw 32-bit addressing
+__device__ __forceinline__ u32x4_t buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (u32x4_t){static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, bytes,
+                   0x00020000u};
+}
+
+// 16 bytes a lane from byte offset `off` of the buffer into LDS at
+// `lds_base` + 16*lane (nontemporal: each byte is read once).  No register
+// receives data, so nothing in flight can be overwritten; the caller waits
+// with an explicit vmcnt before the barrier that publishes the tile.
+// `rs` and `lds_base` are wave-uniform; readfirstlane puts them in SGPRs.
+__device__ __forceinline__ void dma16(u32x4_t rs, const uint8_t* lds_base, uint32_t off) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const uint8_t*)(lds_base))));
+  u32x4_t rsu;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsu[i] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rs[i]));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(la), "v"(off), "s"(rsu)
+               : "memory", "m0");
 }
 
 }  // namespace
 
-template <int D, int GM>
-__global__ __launch_bounds__(64, DecodeOccupancy<GM>::value) void decode_split_kernel(
-    DecodeParams p, const int32_t* __restrict__ page_table) {
-  using S = DecodeShape<D>;
-  constexpr int TILE = S::TILE, LPT = S::LPT, HPC = S::HPC, CPL = S::CPL, KROW = S::KROW;
+// RB: bytes of the head group's part of a token row (head_group * D * 2).
+// S: LDS stages (tiles in flight while one is computed: S - 1).
+template <int D, int RB, int S>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeParams p) {
+  constexpr int KB = RB >= 2048 ? 8 : (16384 / RB < 64 ? 16384 / RB : 64);  // tokens per tile
+  constexpr int KS = D / 32;                  // k-steps of S^T
+  constexpr int CB = D / 16;                  // 16-channel blocks of O^T
+  constexpr int NB = KB >= 16 ? KB / 16 : 1;  // 16-key blocks per tile
+  constexpr int BK = KB >= 16 ? 16 : KB;      // keys in use per block
+  constexpr int NI = 2 * KB * RB / 1024;      // DMA instructions of 1 KiB per tile (K then V)
+  constexpr int IPW = NI / kWaves;            // ... per wave
+  constexpr int LG_RB = RB == 128 ? 7 : RB == 256 ? 8 : RB == 512 ? 9 : RB == 1024 ? 10 : 11;
+  // 16-byte columns of staged rows are XOR-permuted by row when a row spans
+  // whole 256-byte bank windows: K reads of 16 rows at one column, and the V
+  // transpose reads of 8 rows at one 32-byte piece, then hit distinct banks
+  constexpr bool SWZ = (RB & 255) == 0;
+  static_assert(IPW * kWaves == NI && KB * RB * 2 <= kStageBytes, "tile shape");
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int r = blockIdx.z;
-  const int lane = threadIdx.x;
+  static_assert(S >= 2 && S <= 4, "stages");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[S > 2 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[S > 3 ? kStageBytes : 16];
+  __shared__ int32_t slot_of[kDecodeWindow];
+  __shared__ int32_t pre[kDecodeBatch + 1];  // token prefix sums of the requests
+  __shared__ int32_t wave_tot[kWaves];
+
+  const int wg = blockIdx.x;
+  const int grp = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.group;
+  const int hg = p.head_group;
   const int Hq = p.num_kv_heads * G;
-  // a length above max_seq_len breaks the caller's contract; clamp it so
-  // that no page_table entry past the row's bound is read.  In a mixed
-  // batch only the rows with one new token are decoded here, and their
-  // q / out row is the request's first row of the batch.
-  int L;
-  int64_t io_row = r;
-  if (p.mixed_cu) {
-    if (p.mixed_extend[r] != 1) return;
-    L = min(p.mixed_prefix[r] + 1, p.max_seq_len);
-    io_row = p.mixed_cu[r];
-  } else {
-    L = min(p.seq_lens[r], p.max_seq_len);
-  }
+  const int B = p.batch;
 
-  if (L <= 0) {  // padding row: zeros, no KV read
-    if (s == 0) {
-      uint16_t* o = p.out + (io_row * Hq + g * G) * D;
-      for (int i = lane; i < G * LPT; i += 64) reinterpret_cast<uint4*>(o)[i] = make_uint4(0, 0, 0, 0);
+  // ---- lengths, rounded up to whole tiles, and their prefix sums: with
+  // ranges of whole tiles, every range boundary falls on a tile boundary of
+  // its request, so a tile never straddles two pages of a request whose page
+  // size is a multiple of KB.  A length above max_seq_len breaks the
+  // caller's contract and is clamped, so that no page_table entry past the
+  // row's bound is read.  In a mixed batch only the rows with one new token
+  // are decode rows (length prefix + 1); the others have none here.
+  {
+    constexpr int RPT = kDecodeBatch / kThreads;  // requests per thread
+    int lens[RPT];
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = tid * RPT + j;
+      int L = 0;
+      if (r < B) {
+        if (p.mixed_cu)
+          L = p.mixed_extend[r] == 1 ? min(p.mixed_prefix[r] + 1, p.max_seq_len) : 0;
+        else
+          L = min(p.seq_lens[r], p.max_seq_len);
+      }
+      lens[j] = (max(L, 0) + KB - 1) / KB * KB;  // whole tiles
+      run += lens[j];
     }
-    return;
+    int incl = run;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int excl = incl - run;
+    int total = 0;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      if (x < w) excl += wave_tot[x];
+      total += wave_tot[x];
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      pre[tid * RPT + j] = excl;
+      excl += lens[j];
+    }
+    if (tid == 0) pre[kDecodeBatch] = total;
+    __syncthreads();
   }
-  const int nch = (L + p.chunk - 1) / p.chunk;
-  if (s >= nch) return;
+  const int T = pre[B];
 
-  __shared__ uint4 k_lds[TILE * KROW / 4];
-  __shared__ uint4 q_lds[GM * LPT];
-  __shared__ uint32_t p_lds[(TILE / 2) * GM];
+  // ---- padding rows (seq_len 0): zeros, no KV read
+  if (!p.mixed_cu) {
+    for (int r = wg; r < B; r += gridDim.x) {
+      if (pre[r + 1] == pre[r]) {
+        uint4* o = reinterpret_cast<uint4*>(p.out + (static_cast<int64_t>(r) * Hq + grp * hg * G) * D);
+        for (int i = tid; i < hg * G * D / 8; i += kThreads) o[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
 
-  // heads G .. GM-1 (a group size that is not a power of two) run on zero
-  // queries and are never written
-  const uint16_t* qrow = p.q + io_row * p.q_stride + static_cast<int64_t>(g) * G * D;
-  for (int i = lane; i < GM * LPT; i += 64)
-    q_lds[i] = (i < G * LPT) ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
+  // ---- this workgroup's token range [a0, b0)
+  const int per = (max(kDecodeMinTokens, static_cast<int>((static_cast<int64_t>(T) + gridDim.x - 1) / gridDim.x)) +
+                   KB - 1) / KB * KB;
+  const int a0 = wg * per;
+  if (a0 >= T) return;
+  const int b0 = min(T, a0 + per);
 
-  const int32_t* pt = page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
-  const int ps = p.page_size;
-  const int sh = p.page_shift;
   const uint32_t row_bytes = static_cast<uint32_t>(p.num_kv_heads) * D * 2;
-  const uint32_t head_off = static_cast<uint32_t>(g) * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(p.k_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(p.v_cache + static_cast<int64_t>(g) * D, p.half_bytes - head_off);
+  const uint32_t grp_off = static_cast<uint32_t>(grp) * RB;
+  const u32x4_t krs = buffer_words(p.k_cache, p.half_bytes);
+  const u32x4_t vrs = buffer_words(p.v_cache, p.half_bytes);
 
-  const int t_begin = s * p.chunk;
-  const int t_end = min(L, t_begin + p.chunk);
-  const int cw = lane % CPL;  // this lane's word of a token row (channels 2cw, 2cw+1)
-  const int qt = lane >> 1;   // q.K layout: token of the tile
-  const int hf = lane & 1;    //              half of the channels
+  // wave w computes kv head g; lane: head column h (valid below G), key
+  // group n (keys 4n .. 4n+3 of a 16-key block)
+  const int g = grp * hg + w;
+  const bool computes = w < hg;
+  const int h = lane & 15;
+  const int n = lane >> 4;
+  const float c2 = p.scale_log2;
+  // per-lane LDS read offsets: K operand (row h of a block, column 4ks + n
+  // of the head) and V transpose read (row 4n + j, 8 bytes at channel
+  // 16cb + 4q of the head, j = (lane&15)/4, q = lane&3)
+  const int kcol0 = w * D / 8 + n;
+  const int vj = (lane & 15) >> 2;
+  const int vq = lane & 3;
 
-  float m_run[GM], l_run[GM], acc[GM][2];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-    acc[h][0] = acc[h][1] = 0.f;
-  }
-  __syncthreads();
-
-  uint16_t* p16 = reinterpret_cast<uint16_t*>(p_lds);
-  uint32_t* k_words = reinterpret_cast<uint32_t*>(k_lds);
-
-  // lane t (mod TILE) returns the byte offset of token t0 + t's row in the
-  // K/V sub-tensor; past the end, the last valid token again (in-bounds
-  // data, weighted by an exact zero below)
-  auto tile_offsets = [&](int t0) -> uint32_t {
-    const int n = min(TILE, t_end - t0);
-    const int tok = t0 + min(lane & (TILE - 1), n - 1);
-    int slot;
-    if (sh >= 0) {
-      slot = (pt[tok >> sh] << sh) + (tok & (ps - 1));
-    } else {
-      const int pg = tok / ps;
-      slot = pt[pg] * ps + (tok - pg * ps);
-    }
-    return static_cast<uint32_t>(min(max(slot, 0), p.num_slots - 1)) * row_bytes;
+  auto stage = [&](auto kc) __attribute__((always_inline)) -> const uint8_t* {
+    constexpr int K = decltype(kc)::value;
+    if constexpr (K == 0) return st0;
+    else if constexpr (K == 1) return st1;
+    else if constexpr (K == 2) return st2;
+    else return st3;
   };
-  uint32_t off_cur = tile_offsets(t_begin);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += TILE) {
-    const int n = min(TILE, t_end - t0);
-    // page ids of the next tile go out now, so their latency hides behind
-    // this tile
-    const uint32_t off_next = (t0 + TILE < t_end) ? tile_offsets(t0 + TILE) : 0u;
-    // one row load per token, at the token's wave-uniform byte offset
-    uint32_t kw[TILE], vw[TILE];
+  // DMA: wave w issues instructions w*IPW .. w*IPW+IPW-1 of tile t of the
+  // window (the first NI/2 fill the K tile, the rest the V tile).  All
+  // slots are read before the first DMA goes out: each DMA is a compiler
+  // barrier for memory.
+  auto issue = [&](int t, const uint8_t* st) __attribute__((always_inline)) {
+    uint32_t off[IPW];
 #pragma unroll
-    for (int t = 0; t < TILE; ++t)
-      kw[t] = __builtin_amdgcn_raw_buffer_load_b32(krs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), kStream);
-#pragma unroll
-    for (int t = 0; t < TILE; ++t)
-      vw[t] = __builtin_amdgcn_raw_buffer_load_b32(vrs, cw * 4, __builtin_amdgcn_readlane(off_cur, t), kStream);
-    if (lane < CPL) {
-#pragma unroll
-      for (int t = 0; t < TILE; ++t) k_words[t * KROW + cw] = kw[t];
+    for (int k = 0; k < IPW; ++k) {
+      const int i = w * IPW + k;
+      const bool mat = i >= NI / 2;
+      const int o = (i - (mat ? NI / 2 : 0)) * 1024 + 16 * lane;  // byte of the matrix tile
+      const int row = o >> LG_RB;
+      const int pcol = (o & (RB - 1)) >> 4;
+      const int lcol = pcol ^ (SWZ ? (mat ? ((row & 7) << 1) : (row & 15)) : 0);
+      off[k] = static_cast<uint32_t>(slot_of[t * KB + row]) * row_bytes + grp_off + lcol * 16;
     }
-    __syncthreads();
-
-    // q.K: lanes 2t and 2t+1 hold token t's two halves.  Each head's q
-    // broadcasts are issued only once the previous head's sum exists (an
-    // empty asm ties the LDS offset to it): the scheduler would otherwise
-    // hoist every head's q reads at once and spill them.
-    uint4 kk[HPC];
 #pragma unroll
-    for (int cc = 0; cc < HPC; ++cc) kk[cc] = k_lds[qt * (KROW / 4) + hf * HPC + cc];
-    float sc[GM];
-    int qoff = hf * HPC;
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h > 0) asm volatile("" : "+v"(qoff) : "v"(sc[h - 1]));
-      else asm volatile("" : "+v"(qoff));
-      float a = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < HPC; ++cc) {
-        const uint4 qq = q_lds[qoff + h * LPT + cc];
-        a = dot2_bf16(kk[cc].x, qq.x, a);
-        a = dot2_bf16(kk[cc].y, qq.y, a);
-        a = dot2_bf16(kk[cc].z, qq.z, a);
-        a = dot2_bf16(kk[cc].w, qq.w, a);
-      }
-      sc[h] = a;
+    for (int k = 0; k < IPW; ++k) {
+      const int i = w * IPW + k;
+      const bool mat = i >= NI / 2;
+      dma16(mat ? vrs : krs, st + (mat ? KB * RB : 0) + (i - (mat ? NI / 2 : 0)) * 1024, off[k]);
     }
+  };
 
-    const bool valid = qt < n;
+  for (int r = [&] {
+         // the request holding token a0: the last r with pre[r] <= a0
+         int lo = 0, hi = B;
+         while (hi - lo > 1) {
+           const int mid = (lo + hi) >> 1;
+           if (pre[mid] <= a0) lo = mid; else hi = mid;
+         }
+         return lo;
+       }();
+       r < B && pre[r] < b0; ++r) {
+    const int first = pre[r] / per;  // the workgroups holding request r
+    const int pieces = (pre[r + 1] - 1) / per - first + 1;
+    // this piece: tokens [sa, sb) of request r (both whole tiles; tokens past
+    // the request's real length are masked)
+    const int L = p.mixed_cu ? min(p.mixed_prefix[r] + 1, p.max_seq_len) : min(p.seq_lens[r], p.max_seq_len);
+    const int sa = max(a0, pre[r]) - pre[r];
+    const int sb = min(min(b0, pre[r + 1]) - pre[r], L);
+    if (sb <= sa) continue;
+    const int64_t io_row = p.mixed_cu ? p.mixed_cu[r] : r;
+    // the merge finds a split request's pieces here
+    if (wg == first && tid == 0) p.ws_map[r] = make_int2(first + r, pieces);
+
+    bf16x8_t qop[KS];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float full = sc[h] + dpp_mov<kDppXor1>(sc[h]);
-      const float x = valid ? full * p.scale_log2 : -INFINITY;
-      const float mnew = fmaxf(m_run[h], wave_max(x));
-      const float alpha = fast_exp2(m_run[h] - mnew);
-      const uint16_t pb = f32_to_bf16(fast_exp2(x - mnew));
-      // both lanes of a token hold the same p: count it once, store it
-      // from both (same value)
-      l_run[h] = l_run[h] * alpha + (hf ? 0.f : bf16_to_f32(pb));
-      m_run[h] = mnew;
-      acc[h][0] *= alpha;
-      acc[h][1] *= alpha;
-      p16[((qt >> 1) * GM + h) * 2 + (qt & 1)] = pb;
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(0.f);
+      if (computes && h < G)
+        qop[ks] = *reinterpret_cast<const bf16x8_t*>(p.q + io_row * p.q_stride +
+                                                     static_cast<int64_t>(g * G + h) * D + ks * 32 + 8 * n);
     }
-    __syncthreads();
+    // the q operands are redefined by an empty asm once their loads are
+    // done: the waitcnt pass would otherwise keep them pending and make the
+    // first MFMA of every tile wait for the DMA in flight
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
 
-    // p.V on token pairs (2j, 2j+1)
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4_t o[CB];
 #pragma unroll
-    for (int j = 0; j < TILE / 2; ++j) {
-      const uint32_t lo = pair_lo(vw[2 * j], vw[2 * j + 1]);
-      const uint32_t hi = pair_hi(vw[2 * j], vw[2 * j + 1]);
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        const uint32_t pp = p_lds[j * GM + h];
-        acc[h][0] = dot2_bf16(lo, pp, acc[h][0]);
-        acc[h][1] = dot2_bf16(hi, pp, acc[h][1]);
-      }
-    }
-    __syncthreads();  // k_lds / p_lds are rewritten by the next tile
-    off_cur = off_next;
-  }
+    for (int cb = 0; cb < CB; ++cb) o[cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  float l_tot[GM];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) l_tot[h] = wave_sum(l_run[h]);
-  if (nch == 1) {
-    if (lane < CPL) {
-      uint16_t* o = p.out + (io_row * Hq + g * G) * D + 2 * cw;
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const float inv = 1.f / l_tot[h];
-          *reinterpret_cast<uint32_t*>(o + h * D) = pack_bf16(acc[h][0] * inv, acc[h][1] * inv);
+    const int32_t* pt = p.page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
+    for (int w0 = sa; w0 < sb; w0 += kDecodeWindow) {
+      const int ntok = min(kDecodeWindow, sb - w0);
+      const int ntiles = (ntok + KB - 1) / KB;
+      // slots of the window's tokens (tokens past its end repeat the last
+      // one: valid rows, masked below).  Every wave is done with the slot
+      // table and the stages of the previous window.
+      __syncthreads();
+      {
+        const int ps = p.page_size;
+        for (int i = tid; i < ntiles * KB; i += kThreads) {
+          const int tok = w0 + min(i, ntok - 1);
+          const int pg = tok / ps;
+          const int sl = pt[pg] * ps + (tok - pg * ps);
+          slot_of[i] = min(max(sl, 0), p.num_slots - 1);
         }
       }
-    }
-    return;
-  }
-  const int64_t base = (static_cast<int64_t>(r) * p.max_chunks + s) * (Hq + 1) + g * G;
-  if (lane < CPL) {
+      __syncthreads();
+
+      auto compute = [&](int t, const uint8_t* kt) __attribute__((always_inline)) {
+        const uint8_t* vt = kt + KB * RB;
+        const int nvalid = ntok - t * KB;  // keys of this tile inside the window
+        // blocks one after another (unrolled, the blocks' operands would not
+        // fit the 128 registers that two workgroups per CU leave a lane)
+#pragma unroll 1
+        for (int b = 0; b < NB; ++b) {
+          // ---- S^T = K Q^T for one block of keys
+          const bool krow_ok = h < BK;
+          const int krow = b * 16 + (krow_ok ? h : 0);
+          const int kx = SWZ ? (krow & 15) : 0;
+          f32x4_t sc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G)
-        *reinterpret_cast<float2*>(p.ws_o + (base + h) * D + 2 * cw) = make_float2(acc[h][0], acc[h][1]);
-    }
-  }
-  if (lane == 0) {
+          for (int ks = 0; ks < KS; ++ks) {
+            bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kt + krow * RB + ((kcol0 + 4 * ks) ^ kx) * 16);
+            if (!krow_ok) {
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        p.ws_ml[(base + h) * 2 + 0] = m_run[h];
-        p.ws_ml[(base + h) * 2 + 1] = l_tot[h];
+              for (int e = 0; e < 8; ++e) ka[e] = static_cast<__bf16>(0.f);
+            }
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[ks], sc, 0, 0, 0);
+          }
+          // keys b*16 + 4n + e of head h; past the block's keys or the window: masked
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * n + e >= BK || b * 16 + 4 * n + e >= nvalid) sc[e] = -INFINITY;
+          // ---- online softmax, log2 domain, on x = s * scale * log2(e)
+          float pr[4];
+          float lsum = 0.f;
+          auto probabilities = [&](float mref) __attribute__((always_inline)) {
+            lsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pr[e] = fast_exp2(__builtin_fmaf(sc[e], c2, -mref));
+              lsum += pr[e];
+            }
+          };
+          bool slow = m_run == -INFINITY;
+          if (__builtin_amdgcn_ballot_w64(slow) == 0) {
+            probabilities(m_run);
+            slow = !(lsum <= kSumLimit);  // also catches inf
+          }
+          if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+            // block maximum of head h over its 4 lane groups
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = xor32_max(mx) * c2;  // scale > 0: the maximum commutes with it
+            const bool move = mx > m_run + kMaxSlack;
+            const float mnew = move ? mx : m_run;
+            const float alpha = fast_exp2(m_run - mnew);
+            probabilities(mnew);
+            m_run = mnew;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+              l_run *= alpha;
+#pragma unroll
+              for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+            }
+          }
+          // ---- P as a bf16 value plus its bf16 remainder
+          const uint32_t h01 = pack_bf16(pr[0], pr[1]);
+          const uint32_t h23 = pack_bf16(pr[2], pr[3]);
+          const uint32_t l01 = pack_bf16(pr[0] - __uint_as_float(h01 << 16),
+                                         pr[1] - __uint_as_float(h01 & 0xFFFF0000u));
+          const uint32_t l23 = pack_bf16(pr[2] - __uint_as_float(h23 << 16),
+                                         pr[3] - __uint_as_float(h23 & 0xFFFF0000u));
+          constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+          l_run = dot2_bf16(h01, kOnes,
+                            dot2_bf16(h23, kOnes, dot2_bf16(l01, kOnes, dot2_bf16(l23, kOnes, l_run))));
+          const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(h01, h23, l01, l23));
+          // ---- O^T += V^T P^T: the lane's 4 keys of channel 16cb + h, twice
+          const bool vrow_ok = 4 * n < BK;
+          const int vrow = b * 16 + (vrow_ok ? 4 * n + vj : vj);
+          const int vx = SWZ ? ((vrow & 7) << 1) : 0;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            i16x4_t v4 = lds_read_tr16(vt + vrow * RB + (((w * D / 8 + 2 * cb) ^ vx) + (vq >> 1)) * 16 +
+                                       8 * (vq & 1));
+            if (!vrow_ok) v4 = (i16x4_t){0, 0, 0, 0};
+            const bf16x8_t va =
+                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v4, v4, 0, 1, 2, 3, 0, 1, 2, 3));
+            o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, o[cb], 0, 0, 0);
+          }
+        }
+      };
+
+      // S stages: tiles t+1 .. t+S-1 land while tile t is computed
+#pragma unroll
+      for (int t = 0; t < S - 1; ++t)
+        if (t < ntiles)
+          issue(t, t == 0 ? st0 : t == 1 ? stage(std::integral_constant<int, 1>{})
+                                         : stage(std::integral_constant<int, 2 % S>{}));
+      auto step = [&](int t, auto kc) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value;
+        // tile t has landed for every wave (S-2 younger tiles may stay in
+        // flight), and every wave is done with tile t-1, whose stage tile
+        // t+S-1 now fills
+        if (t + S - 2 < ntiles) {
+          if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((S - 2) * IPW) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        if (t + S - 1 < ntiles) issue(t + S - 1, stage(std::integral_constant<int, (K + S - 1) % S>{}));
+        if (computes) compute(t, stage(kc));
+      };
+      for (int t = 0; t < ntiles; t += S) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+        if constexpr (S > 2)
+          if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2 % S>{});
+        if constexpr (S > 3)
+          if (t + 3 < ntiles) step(t + 3, std::integral_constant<int, 3 % S>{});
       }
+    }
+
+    // ---- the piece's result: the head's sum over its 4 lane groups
+    float l_tot = l_run + shfl_xor_f(l_run, 16);
+    l_tot = xor32_sum(l_tot);
+    if (pieces == 1) {
+      if (computes && h < G) {
+        const float inv = 1.f / l_tot;
+        uint16_t* op = p.out + (io_row * Hq + g * G + h) * D + 4 * n;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          uint2 wv;
+          wv.x = pack_bf16(o[cb][0] * inv, o[cb][1] * inv);
+          wv.y = pack_bf16(o[cb][2] * inv, o[cb][3] * inv);
+          *reinterpret_cast<uint2*>(op + cb * 16) = wv;
+        }
+      }
+      continue;
+    }
+    if (computes && h < G) {
+      const int64_t u = static_cast<int64_t>(wg + r) * Hq + g * G + h;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        *reinterpret_cast<f32x4_t*>(p.ws_o + u * D + cb * 16 + 4 * n) = o[cb];
+      if (n == 0) *reinterpret_cast<float2*>(p.ws_ml + u * 2) = make_float2(m_run, l_tot);
     }
   }
 }
 
-// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the chunks s of
-// one (request, q head), with M the largest chunk maximum.  One wave per
-// (request, q head): lane l owns float4 piece l % (D/4) of the head and the
-// chunks s = l / (D/4) (mod 64 / (D/4)); the lanes that share a piece are
-// joined by exchanges 32 (and 16) lanes apart.
-constexpr int kMergeThreads = 64;
-
+// out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i over the pieces i of
+// one (request, q head) that the decode kernel split, with M the largest
+// piece maximum.  One wave per (request, q head): lane l owns float4 piece
+// l % (D/4) of the head and the pieces i = l / (D/4) (mod 64 / (D/4)); the
+// lanes that share a float4 are joined by exchanges 32 (and 16) lanes apart.
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
-  constexpr int QPH = D / 4;          // float4 pieces per head
-  constexpr int NH = 64 / QPH;        // lanes per piece (chunk phases)
-  const int h = blockIdx.x;           // q head
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+  constexpr int QPH = D / 4;    // float4 pieces per head
+  constexpr int NPH = 64 / QPH; // lanes per float4 (piece phases)
+  const int head = blockIdx.x;
   const int r = blockIdx.y;
   const int lane = threadIdx.x;
-  int L;
-  int64_t io_row = r;
-  if (p.mixed_cu) {
-    if (p.mixed_extend[r] != 1) return;
-    L = min(p.mixed_prefix[r] + 1, p.max_seq_len);
-    io_row = p.mixed_cu[r];
-  } else {
-    L = min(p.seq_lens[r], p.max_seq_len);
-  }
+  // requests with no tokens (padding, or the extend rows of a mixed batch)
+  // have no piece map of this call
+  const int L = p.mixed_cu ? (p.mixed_extend[r] == 1 ? p.mixed_prefix[r] + 1 : 0) : p.seq_lens[r];
   if (L <= 0) return;
-  const int nch = (L + p.chunk - 1) / p.chunk;
-  if (nch <= 1) return;
+  const int2 map = p.ws_map[r];
+  const int pieces = map.y;
+  if (pieces <= 1) return;  // written by the decode kernel itself
   const int Hq = p.num_kv_heads * p.group;
-  // chunk s at base + s*(Hq+1): one unit of padding per chunk keeps the
-  // chunk stride off powers of two
-  const int64_t base = static_cast<int64_t>(r) * p.max_chunks * (Hq + 1) + h;
-  const int64_t row = Hq + 1;
-  const int cq = lane % QPH;
+  const int64_t u0 = static_cast<int64_t>(map.x) * Hq + head;  // piece i at u0 + i*Hq
+  const int c4 = lane % QPH;
   const int ph = lane / QPH;
-
   float mx = -INFINITY;
-  for (int s = lane; s < nch; s += 64) mx = fmaxf(mx, p.ws_ml[(base + s * row) * 2]);
+  for (int i = lane; i < pieces; i += 64) mx = fmaxf(mx, p.ws_ml[(u0 + static_cast<int64_t>(i) * Hq) * 2]);
   mx = wave_max(mx);
-
   float den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-  for (int s = ph; s < nch; s += NH) {
-    const int64_t u = base + s * row;
+  for (int i = ph; i < pieces; i += NPH) {
+    const int64_t u = u0 + static_cast<int64_t>(i) * Hq;
     const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + u * 2);
-    const float w = fast_exp2(ml.x - mx);
-    den += w * ml.y;
-    const float4 o = reinterpret_cast<const float4*>(p.ws_o + u * D)[cq];
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
+    const float wgt = fast_exp2(ml.x - mx);
+    den += wgt * ml.y;
+    const float4 v = reinterpret_cast<const float4*>(p.ws_o + u * D)[c4];
+    acc.x += wgt * v.x;
+    acc.y += wgt * v.y;
+    acc.z += wgt * v.z;
+    acc.w += wgt * v.w;
   }
-  // join the NH lanes of each piece (their den values differ per phase)
 #pragma unroll
   for (int off = 32; off >= QPH; off >>= 1) {
     den += shfl_xor_f(den, off);
@@ -335,46 +500,53 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     acc.w += shfl_xor_f(acc.w, off);
   }
   if (lane < QPH) {
+    const int64_t io_row = p.mixed_cu ? p.mixed_cu[r] : r;
     const float inv = 1.f / den;
     uint2 wv;
     wv.x = pack_bf16(acc.x * inv, acc.y * inv);
     wv.y = pack_bf16(acc.z * inv, acc.w * inv);
-    *reinterpret_cast<uint2*>(p.out + (io_row * Hq + h) * D + 4 * lane) = wv;
+    *reinterpret_cast<uint2*>(p.out + (io_row * Hq + head) * D + 4 * lane) = wv;
   }
 }
 
-template <int D, int GM>
-static void launch_decode_t(const DecodeParams& p, int batch, hipStream_t stream) {
-  // an odd grid width: with a multiple of 8 chunk columns every chunk
-  // index lands on the same XCD in every row (workgroups are dealt to the 8
-  // XCDs round-robin), which measured up to 1.6x slower
-  const dim3 grid(p.max_chunks | 1, p.num_kv_heads, batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, GM>), grid, dim3(64), 0, stream, p, p.page_table);
-  if (p.max_chunks > 1) {
-    const dim3 mgrid(p.num_kv_heads * p.group, batch);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(kMergeThreads), 0, stream, p);
+namespace {
+
+template <int D, int S>
+void launch_decode_s(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(kDecodeGrid, p.num_kv_heads / p.head_group);
+  switch (p.head_group) {
+    case 8:
+      hipLaunchKernelGGL((decode_kernel<D, 8 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      break;
+    case 4:
+      hipLaunchKernelGGL((decode_kernel<D, 4 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((decode_kernel<D, 2 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_kernel<D, D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      break;
   }
 }
 
 template <int D>
-static void launch_decode_d(const DecodeParams& p, int batch, hipStream_t stream) {
-  if (p.group <= 1)
-    launch_decode_t<D, 1>(p, batch, stream);
-  else if (p.group <= 2)
-    launch_decode_t<D, 2>(p, batch, stream);
-  else if (p.group <= 4)
-    launch_decode_t<D, 4>(p, batch, stream);
-  else if (p.group <= 8)
-    launch_decode_t<D, 8>(p, batch, stream);
-  else
-    launch_decode_t<D, 16>(p, batch, stream);
+void launch_decode_d(const DecodeParams& p, hipStream_t stream) {
+  // two stages: with two 8-wave workgroups per CU (LDS and registers allow
+  // no more), one tile of each is in flight while the other is computed;
+  // measured faster than three or four stages at one workgroup per CU
+  launch_decode_s<D, 2>(p, stream);
+  const dim3 mgrid(p.num_kv_heads * p.group, p.batch);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), mgrid, dim3(64), 0, stream, p);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int batch, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
   if (head_dim == 128)
-    launch_decode_d<128>(p, batch, stream);
+    launch_decode_d<128>(p, stream);
   else
-    launch_decode_d<64>(p, batch, stream);
+    launch_decode_d<64>(p, stream);
   return hipGetLastError();
 }
 

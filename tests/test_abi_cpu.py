@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msgl.h")
 
 OK, NULL, SHAPE, UNSUP, WS, RANGE, HIP = 0, 1, 2, 3, 4, 5, 6
-FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
 
 
 def _lib():
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.msgl_abi_version() == 1
+    assert lib.msgl_abi_version() == 2
     for s in range(7):
         assert lib.msgl_status_string(s)
     assert lib.msgl_status_string(99) == b"unknown status"
@@ -61,17 +61,32 @@ def _pool(**kw):
                       p["num_kv_heads"], p["head_dim"])
 
 
+def _ws_bytes(batch, hq, d, max_len):
+    """A piece map (int2 per request), then per launch of up to 2048
+    requests the fp32 partials of its pieces: at most
+    min(512 ranges, ceil(b * max_len / 64)) + b."""
+    a256 = lambda x: -(-x // 256) * 256
+    pieces = 0
+    for b0 in range(0, batch, 2048):
+        b = min(2048, batch - b0)
+        pieces += min(512, -(-b * max_len // 64)) + b
+    return a256(batch * 8) + a256(pieces * hq * d * 4) + pieces * hq * 8
+
+
 def test_workspace_size_is_host_arithmetic():
+    # (batch, num_qo_heads, head_dim, max_seq_len, page_size)
     lib = _lib()
     f = lib.msgl_paged_decode_workspace_size
-    assert f(64, 32, 8, 128, 384) == 0  # one split: no partials
-    n = f(64, 32, 8, 128, 4096)
-    chunks = -(-4096 // 384)
-    units = 64 * chunks * (32 + 1)  # one padding unit per (request, chunk)
-    assert n == ((units * 128 * 4 + 255) // 256) * 256 + units * 8
-    assert f(-1, 32, 8, 128, 4096) == 0
+    n = f(64, 32, 128, 4096, 16)
+    assert n == _ws_bytes(64, 32, 128, 4096)
+    assert f(8, 32, 128, 512, 16) == _ws_bytes(8, 32, 128, 512)  # 72 pieces
+    assert f(3000, 32, 128, 1000, 1) == _ws_bytes(3000, 32, 128, 1000)  # two launches
+    assert f(0, 32, 128, 4096, 16) == 0
+    assert f(-1, 32, 128, 4096, 16) == 0 and f(4, 32, 128, 4096, 0) == 0
+    # the page size does not change the layout
+    assert f(64, 32, 128, 4096, 1) == n == f(64, 32, 128, 4096, 13)
     # monotone in batch and length, so one allocation serves smaller calls
-    assert f(32, 32, 8, 128, 4096) <= n and f(64, 32, 8, 128, 2048) <= n
+    assert f(32, 32, 128, 4096, 16) <= n and f(64, 32, 128, 2048, 16) <= n
 
 
 def test_store_kv_rejects_bad_arguments_without_launch():

@@ -145,7 +145,7 @@ def test_eager_calls_capture_in_a_torch_graph_over_layers():
     q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((B, hkv, d), dtype=torch.bfloat16, device="cuda")
     v = torch.zeros_like(k)
-    ws = torch.empty(msgl.paged_decode_workspace_size(B, hq, hkv, d, cap), dtype=torch.uint8,
+    ws = torch.zeros(max(msgl.paged_decode_workspace_size(B, hq, d, cap, ps), 256), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(NL)]
 

@@ -640,7 +640,7 @@ def test_decode_workspace_reuse_and_split_override(monkeypatch):
     msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
     pool_bits = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
     ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, ph.seq_lens)
-    need = msgl.paged_decode_workspace_size(64, 16, 2, 128, 8192)
+    need = msgl.paged_decode_workspace_size(64, 16, 128, 8192, 16)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for split in ("64", "256", "1024"):
         monkeypatch.setenv("MSGL_DECODE_SPLIT", split)
