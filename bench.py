@@ -316,13 +316,14 @@ def mixed_stats(msgl, dev, iters=10):
     return res
 
 
-def other_workloads(msgl, dev, ext_iters=3, dec_iters=20):
+def other_workloads(msgl, dev, ext_iters=3, dec_iters=20, only=None):
     """The two remaining workloads, each as store_kv then attention, timed
     with HIP events on the launch stream (warm caches):
       * chunked prefill: one 32768-token request as 8 extend chunks of 4096
         over the growing prefix (32 q / 8 kv heads, d 128, ps 16, std 0.5);
       * Qwen3-30B-A3B attention geometry decode: 32 q / 4 kv heads, d 128,
         page_size 1, 256 requests with lognormal lengths (sum 824055).
+    `only` names one of them to run alone (for profiles).
     """
     from workloads import config_chunked_prefill, config_qwen3_moe_decode
 
@@ -330,6 +331,8 @@ def other_workloads(msgl, dev, ext_iters=3, dec_iters=20):
         return torch.cuda.Event(enable_timing=True)
 
     res = {}
+    if only not in (None, "chunked_prefill"):
+        return res | qwen_decode_stats(msgl, dev, dec_iters)
     wl = config_chunked_prefill(device=dev)
     preps = [Prepared(wl, ph, dev) for ph in wl.phases]
     for p in preps:  # the pool holds every chunk's rows before timing
@@ -369,7 +372,18 @@ def other_workloads(msgl, dev, ext_iters=3, dec_iters=20):
     }
     del preps, wl
     torch.cuda.empty_cache()
+    if only == "chunked_prefill":
+        return res
+    return res | qwen_decode_stats(msgl, dev, dec_iters)
 
+
+def qwen_decode_stats(msgl, dev, dec_iters):
+    from workloads import config_qwen3_moe_decode
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    res = {}
     wl = config_qwen3_moe_decode(device=dev)
     p = Prepared(wl, wl.phases[0], dev)
     for _ in range(3):
@@ -402,6 +416,41 @@ def other_workloads(msgl, dev, ext_iters=3, dec_iters=20):
     del p, wl
     torch.cuda.empty_cache()
     return res
+
+
+def measured_ceilings(dev, iters=10):
+    """What this GPU sustains, measured in this run beside the spec peaks:
+    a 512 MiB device copy (bytes read + written), a 1 GiB read (torch's sum
+    of bf16 values) and a 8192^3 bf16 GEMM (hipBLASLt through torch)."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3  # s
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    big = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    t_read = timed(lambda: big.sum())
+    del big
+    m = 8192
+    a = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    b = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    t_gemm = timed(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_512MiB_GBs": round(2 * n / t_copy / 1e9, 1),
+            "read_1GiB_GBs": round((1 << 30) / t_read / 1e9, 1),
+            "bf16_gemm_8192_TFLOPs": round(2 * m ** 3 / t_gemm / 1e12, 1)}
 
 
 def graph_vs_eager(msgl, dev, iters=300):
@@ -485,6 +534,9 @@ def main():
                          "only the step's kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode"],
+                    help="time only this workload (store_kv + attention) and print its figures; "
+                         "for profiles of the workloads outside the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -499,6 +551,19 @@ def main():
     from workloads import config_llama3_8b_decode, config_radix_shared_extend
 
     msgl.load_library()
+    if args.only:
+        log(f"{args.only} only")
+        res = other_workloads(msgl, dev, ext_iters=max(1, args.steps), dec_iters=max(1, args.steps),
+                              only=args.only)
+        if args.copy_calibration:
+            src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        print(json.dumps(res), flush=True)
+        return
     log("building workloads on the device")
     wl_dec = config_llama3_8b_decode(device=dev)
     wl_ext = config_radix_shared_extend(device=dev)
@@ -573,8 +638,10 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    alloc = mixed = rope_stats = graph_stats = others = None
+    alloc = mixed = rope_stats = graph_stats = others = ceilings = None
     if not args.step_only:
+        log("measured ceilings (copy, read, bf16 GEMM)")
+        ceilings = measured_ceilings(dev)
         log("device-side page allocation")
         alloc = {"decode_step": alloc_stats(msgl, pd, dev), "extend_step": alloc_stats(msgl, pe, dev)}
         log("mixed decode + extend batch")
@@ -619,7 +686,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "msgl_paged_decode (split-KV decode + merge)",
+            "kernel": "msgl_paged_decode (balanced-range decode + merge)",
             "achieved": round(dec_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -630,6 +697,11 @@ def main():
             "median_launch_us": round(dec_med * 1e3, 3),
             "cold_mall_median_us": round(cold_ms * 1e3, 3),
             "cold_mall_GBs": round(dbytes / (cold_ms * 1e-3) / 1e9, 2),
+            "measured_ceiling": None if ceilings is None else {
+                "copy_GBs": ceilings["copy_512MiB_GBs"],
+                "read_GBs": ceilings["read_1GiB_GBs"],
+                "frac_of_copy": round(dec_gbs / ceilings["copy_512MiB_GBs"], 4),
+                "frac_of_read": round(dec_gbs / ceilings["read_1GiB_GBs"], 4)},
         },
         "roofline_extend": {
             "bound": "mfma",
@@ -642,6 +714,9 @@ def main():
             "algorithmic_flops_per_launch": eflops,
             "avg_launch_us": round(ext_ms * 1e3, 3),
             "median_launch_us": round(ext_med * 1e3, 3),
+            "measured_ceiling": None if ceilings is None else {
+                "bf16_gemm_TFLOPs": ceilings["bf16_gemm_8192_TFLOPs"],
+                "frac_of_gemm": round(ext_tflops / ceilings["bf16_gemm_8192_TFLOPs"], 4)},
         },
         "store_kv": {
             "decode_rows": ph_d.num_tokens,
