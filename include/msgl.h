@@ -152,6 +152,26 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
                               size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_noalloc: msgl_paged_decode for callers that cannot allocate
+ * device memory -- code under graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and result as msgl_paged_decode,
+ * without the workspace: the call uses a device array inside the library
+ * (64 MiB, msgl_paged_decode_noalloc_max_workspace(), one per GPU, held
+ * until the process ends) and allocates nothing.  A call whose
+ * msgl_paged_decode_workspace_size(...) exceeds that limit returns
+ * MSGL_ERR_WORKSPACE before touching the GPU.  Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different
+ * streams not ordered by events, or several threads) race and give wrong
+ * results; order them.
+ */
+size_t msgl_paged_decode_noalloc_max_workspace(void);
+msgl_status msgl_paged_decode_noalloc(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                                      int64_t q_row_stride, void* out, const int32_t* page_table,
+                                      int32_t page_table_stride, const int32_t* table_idx,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
+                                      int32_t max_seq_len, float sm_scale, void* stream);
+
+/*
  * paged_extend: causal prefill/extend over a cached prefix.  Request r has
  * prefix_lens[r] tokens already in the pool (a radix-cache hit or earlier
  * prefill chunks) and extend_lens[r] new tokens, already stored, whose

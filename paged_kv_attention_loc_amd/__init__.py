@@ -30,6 +30,9 @@ __all__ = [
     "msgl_store_kv",
     "msgl_paged_decode",
     "msgl_paged_decode_workspace_size",
+    "msgl_paged_decode_noalloc",
+    "paged_decode_noalloc",
+    "paged_decode_noalloc_max_workspace",
     "msgl_paged_extend",
     "msgl_debug_gather_kv",
     "store_kv",
@@ -99,6 +102,10 @@ def load_library():
     lib.msgl_paged_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.msgl_paged_decode.restype = I32
     lib.msgl_paged_decode.argtypes = [PP, I32, P, I64, P, P, I32, P, P, I32, I32, I32, F32, P, SZ, P]
+    lib.msgl_paged_decode_noalloc.restype = I32
+    lib.msgl_paged_decode_noalloc.argtypes = [PP, I32, P, I64, P, P, I32, P, P, I32, I32, I32, F32, P]
+    lib.msgl_paged_decode_noalloc_max_workspace.restype = SZ
+    lib.msgl_paged_decode_noalloc_max_workspace.argtypes = []
     lib.msgl_paged_extend.restype = I32
     lib.msgl_paged_extend.argtypes = [PP, I32, P, I64, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
                                       F32, P]
@@ -223,6 +230,38 @@ def msgl_paged_decode(pool: torch.Tensor, layer: int, q: torch.Tensor, page_tabl
         int(max_seq_len), float(sm_scale), ws_ptr, ws_bytes, _stream(q))
     _check(st, "msgl_paged_decode")
     return out
+
+
+def msgl_paged_decode_noalloc(pool: torch.Tensor, layer: int, q: torch.Tensor,
+                              page_table: torch.Tensor, table_idx: torch.Tensor,
+                              seq_lens: torch.Tensor, max_seq_len: int,
+                              sm_scale: Optional[float] = None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_decode with the library's own device scratch instead of a
+    workspace (msgl_paged_decode_noalloc): no device allocation in the call
+    when ``out`` is given.  Calls on one GPU must not overlap in time."""
+    ps = _pool_struct(pool)
+    B, hq, d = q.shape
+    qs = _rows(q, "q", hq, d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D (rows, entries)")
+    st = load_library().msgl_paged_decode_noalloc(
+        ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
+        int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(seq_lens, "seq_lens"), B, hq,
+        int(max_seq_len), float(sm_scale), _stream(q))
+    _check(st, "msgl_paged_decode_noalloc")
+    return out
+
+
+def paged_decode_noalloc_max_workspace() -> int:
+    """Bytes of the device scratch msgl_paged_decode_noalloc draws on."""
+    return int(load_library().msgl_paged_decode_noalloc_max_workspace())
 
 
 def msgl_paged_extend(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
@@ -457,6 +496,7 @@ rope_cos_sin_table = msgl_rope_cos_sin_table
 alloc_pages = msgl_alloc_pages
 paged_mixed = msgl_paged_mixed
 paged_decode = msgl_paged_decode
+paged_decode_noalloc = msgl_paged_decode_noalloc
 paged_decode_workspace_size = msgl_paged_decode_workspace_size
 paged_extend = msgl_paged_extend
 debug_gather_kv = msgl_debug_gather_kv

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -317,6 +318,31 @@ msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q
   return MSGL_OK;
 }
 
+// Allocation-free decode: the workspace comes from this file-scope device
+// array instead of the caller.  Each GPU the library runs on holds its own
+// copy until the process ends; host code reaches a device's copy only
+// through the address hipGetSymbolAddress returns with that device current
+// (the array's name on the host is a stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device.
+msgl_status scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MSGL_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MSGL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSGL_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MSGL_OK;
+}
+
 }  // namespace
 
 // A captured store_kv + decode: the instantiated HIP graph.
@@ -456,6 +482,29 @@ msgl_status msgl_paged_decode(const msgl_kv_pool* pool, int32_t layer, const voi
                                        table_idx, seq_lens, batch, num_qo_heads, max_seq_len,
                                        sm_scale, workspace);
   return hip_status(launch_decode_batches(p, d, static_cast<hipStream_t>(stream)));
+}
+
+size_t msgl_paged_decode_noalloc_max_workspace(void) { return kScratchBytes; }
+
+msgl_status msgl_paged_decode_noalloc(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                                      int64_t q_row_stride, void* out, const int32_t* page_table,
+                                      int32_t page_table_stride, const int32_t* table_idx,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_qo_heads,
+                                      int32_t max_seq_len, float sm_scale, void* stream) {
+  // sizes beyond the scratch array are refused before any HIP call
+  msgl_status st = check_pool(pool, layer);
+  if (st != MSGL_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || num_qo_heads < 1) return MSGL_ERR_SHAPE;
+  if (batch == 0) return MSGL_OK;
+  const size_t need = msgl_paged_decode_workspace_size(batch, num_qo_heads, pool->head_dim,
+                                                       max_seq_len, pool->page_size);
+  if (need > kScratchBytes) return MSGL_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != MSGL_OK) return st;
+  return msgl_paged_decode(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                           table_idx, seq_lens, batch, num_qo_heads, max_seq_len, sm_scale, ws,
+                           kScratchBytes, stream);
 }
 
 msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const void* q,

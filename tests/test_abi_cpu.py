@@ -138,6 +138,23 @@ def test_decode_rejects_bad_arguments_without_launch():
     assert _decode(lib, _pool(num_kv_heads=8, num_pages=1 << 17, page_size=16)) == UNSUP
 
 
+def test_decode_noalloc_refuses_oversize_without_launch():
+    # host arithmetic only: a batch whose workspace exceeds the library's
+    # scratch is refused before any HIP call (this container has no GPU)
+    lib = _lib()
+    p = _pool(num_kv_heads=8)
+    cap = lib.msgl_paged_decode_noalloc_max_workspace()
+    assert cap == 64 << 20
+    big = 8192
+    assert lib.msgl_paged_decode_workspace_size(big, 32, 128, 4096, 16) > cap
+    f = lib.msgl_paged_decode_noalloc
+    assert f(ctypes.byref(p), 0, FAKE, 32 * 128, FAKE, FAKE, 256, FAKE, FAKE, big, 32, 4096, 0.088,
+             None) == WS
+    assert f(None, 0, FAKE, 32 * 128, FAKE, FAKE, 256, FAKE, FAKE, 4, 32, 4096, 0.088, None) == NULL
+    assert f(ctypes.byref(p), 0, FAKE, 32 * 128, FAKE, FAKE, 256, FAKE, FAKE, 0, 32, 4096, 0.088,
+             None) == OK
+
+
 def _extend(lib, pool, **kw):
     a = dict(layer=0, q=FAKE, q_stride=32 * 128, out=FAKE, pt=FAKE, pt_stride=256, ti=FAKE,
              pl=FAKE, el=FAKE, cu=FAKE, batch=2, total=100, max_ext=64, max_len=4096, hq=32,
