@@ -260,15 +260,26 @@ def alloc_stats(msgl, p, dev, iters=50):
 
 
 def mixed_stats(msgl, dev, iters=10):
-    """A mixed batch -- the 64 decode rows of the Llama-3-8B geometry batch
-    (lengths uniform in [512, 4096], seed 2) and 4 chunked-prefill pieces of
-    512 new tokens on 2048-token prefixes -- as one paged_mixed call and as
-    a decode call plus an extend call over the same rows."""
+    """Mixed batches -- the 64 decode rows of the Llama-3-8B geometry batch
+    (lengths uniform in [512, 4096], seed 2) with chunked-prefill pieces of
+    512 new tokens on 2048-token prefixes: one piece (a serving step with a
+    prefill chunk in flight: its tiles leave most CUs to the decode rows)
+    and four (their tiles alone fill every CU).  Each as one paged_mixed
+    call (one attention launch), as a decode call plus an extend call over
+    the same rows, and as a paged_mixed call made of those same launches
+    (MSGL_MIXED_SPLIT=1)."""
+    res = {}
+    for name, n_chunks in (("one_chunk", 1), ("four_chunks", 4)):
+        res[name] = _mixed_case(msgl, dev, n_chunks, iters)
+    return res
+
+
+def _mixed_case(msgl, dev, n_chunks, iters):
     from workloads import build_case
     rng = np.random.default_rng(2)
     L = rng.integers(512, 4096, 64, endpoint=True)
-    P = [int(x) - 1 for x in L] + [2048] * 4
-    E = [1] * 64 + [512] * 4
+    P = [int(x) - 1 for x in L] + [2048] * n_chunks
+    E = [1] * 64 + [512] * n_chunks
     wl = build_case(12, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                     prefix_lens=P, extend_lens=E, device=dev)
     ph = wl.phases[0]
@@ -278,7 +289,7 @@ def mixed_stats(msgl, dev, iters=10):
     q_dec = p.q[torch.from_numpy(ph.cu_extend_lens[dec].astype(np.int64)).to(dev)].contiguous()
     sl_dec = i32(np.asarray(P)[dec] + 1, dev)
     ti_dec = i32(ph.table_idx[dec], dev)
-    ext = np.arange(64, 68)
+    ext = np.arange(64, 64 + n_chunks)
     first = int(ph.cu_extend_lens[64])
     q_ext = p.q[first:].contiguous()
     cu_ext = i32(ph.cu_extend_lens[64:] - first, dev)
@@ -299,8 +310,16 @@ def mixed_stats(msgl, dev, iters=10):
         msgl.paged_extend(p.pool, wl.layer, q_ext, p.pt, ti_ext, pl_ext, el_ext, cu_ext, 512,
                           p.max_len, out=out_ext)
 
-    res = {"decode_rows": 64, "extend_rows": 4, "extend_tokens": 2048}
-    for name, fn in (("mixed_call_us", mixed), ("separate_calls_us", separate)):
+    def mixed_split():
+        os.environ["MSGL_MIXED_SPLIT"] = "1"
+        try:
+            mixed()
+        finally:
+            del os.environ["MSGL_MIXED_SPLIT"]
+
+    res = {"decode_rows": 64, "extend_rows": n_chunks, "extend_tokens": 512 * n_chunks}
+    for name, fn in (("mixed_call_us", mixed), ("separate_calls_us", separate),
+                     ("mixed_split_launches_us", mixed_split)):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -534,7 +553,7 @@ def main():
                          "only the step's kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode"],
+    ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch"],
                     help="time only this workload (store_kv + attention) and print its figures; "
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
@@ -553,8 +572,11 @@ def main():
     msgl.load_library()
     if args.only:
         log(f"{args.only} only")
-        res = other_workloads(msgl, dev, ext_iters=max(1, args.steps), dec_iters=max(1, args.steps),
-                              only=args.only)
+        if args.only == "mixed_batch":
+            res = {"mixed_batch": mixed_stats(msgl, dev, iters=max(1, args.steps))}
+        else:
+            res = other_workloads(msgl, dev, ext_iters=max(1, args.steps),
+                                  dec_iters=max(1, args.steps), only=args.only)
         if args.copy_calibration:
             src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
             dst = torch.empty_like(src)

@@ -328,9 +328,14 @@ msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph);
  *   - every other row goes through the extend kernel (rows with
  *     extend_lens[r] == 0 produce nothing).
  * The result equals paged_extend on the same batch within the attention
- * tolerance; the decode rows equal paged_decode on those rows exactly.
- * Three launches on `stream` (decode, merge, extend); calls sharing a
- * workspace must not overlap.
+ * tolerance; the decode rows equal paged_decode on those rows exactly, and
+ * the extend rows equal paged_extend on the batch exactly.
+ * Launches on `stream`: with batch <= 2048 and a power-of-two page_size,
+ * one attention launch (extend tiles first, then the decode ranges, in
+ * one grid) and the merge of split decode rows; otherwise decode, merge
+ * and extend launches (also when MSGL_MIXED_SPLIT=1 is set);
+ * max_extend_len <= 1 (decode rows only) runs decode and merge alone.
+ * Calls sharing a workspace must not overlap.
  */
 msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void* q,
                              int64_t q_row_stride, void* out, const int32_t* page_table,

@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsgl.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "store_kv.hip", "decode.hip", "extend.hip", "rope.hip", "alloc.hip"]
+SOURCES = ["abi.hip", "store_kv.hip", "decode.hip", "extend.hip", "mixed.hip", "rope.hip", "alloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -563,13 +563,24 @@ msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void
   pd.mixed_prefix = prefix_lens;
   pd.mixed_extend = extend_lens;
   pd.mixed_cu = cu_extend_lens;
-  st = hip_status(launch_decode_batches(pd, d, s));
-  if (st != MSGL_OK) return st;
+  if (max_extend_len <= 1) return hip_status(launch_decode_batches(pd, d, s));  // decode rows only
   // the other rows: causal extend
   const ExtendParams pe = extend_params(pool, layer, q, q_row_stride, out, page_table,
                                         page_table_stride, table_idx, prefix_lens, extend_lens,
                                         cu_extend_lens, num_qo_heads, static_cast<int32_t>(mtiles),
                                         max_extend_len, max_seq_len, sm_scale, 1);
+  // one launch: a row of E > 1 new tokens has ceil(E*G/256) row tiles, so
+  // the batch has at most total*G/256 + batch of them
+  const int64_t G = num_qo_heads / pool->num_kv_heads;
+  const int64_t bound = std::min<int64_t>(static_cast<int64_t>(batch) * mtiles,
+                                          static_cast<int64_t>(total_extend_tokens) * G / 256 + batch);
+  const int64_t blocks = bound * pool->num_kv_heads +
+                         static_cast<int64_t>(kDecodeGrid) * (pool->num_kv_heads / pd.head_group);
+  if (batch <= kDecodeBatch && waves == 8 && pe.page_shift >= 0 && blocks <= INT32_MAX &&
+      !env_on("MSGL_MIXED_SPLIT"))
+    return hip_status(launch_mixed(pd, pe, d, bound, s));
+  st = hip_status(launch_decode_batches(pd, d, s));
+  if (st != MSGL_OK) return st;
   return hip_status(launch_extend(pe, d, batch, waves, s));
 }
 

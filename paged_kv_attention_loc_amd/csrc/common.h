@@ -256,8 +256,15 @@ struct AllocParams {
 // Launchers (defined next to their kernels); return the HIP status.
 hipError_t launch_store_kv(const StoreParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
-// one launch of at most kDecodeBatch requests
+// one launch of at most kDecodeBatch requests (decode, then merge)
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+// the merge of the requests that the decode kernel split
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream);
+// A mixed batch of at most kDecodeBatch requests in one attention launch
+// (8-wave extend workgroups, page_size a power of two), then the merge;
+// ext_tiles_bound bounds the extend row tiles (256 packed rows) of the batch
+hipError_t launch_mixed(const DecodeParams& pd, const ExtendParams& pe, int head_dim,
+                        int64_t ext_tiles_bound, hipStream_t stream);
 // `waves` (4 or 8) sets the query rows per workgroup (32 per wave); the
 // caller sizes p.num_mtiles for it.
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,
