@@ -475,28 +475,25 @@ def measured_ceilings(dev, iters=10):
 def graph_vs_eager(msgl, dev, iters=300):
     """A small decode step -- store_kv of 8 new rows, then decode of 8
     requests of 512 tokens in the Llama-3-8B geometry -- issued as the eager
-    calls and as one launch of a captured decode graph, back to back with
-    one synchronisation at the end (launch overhead dominates at this size)."""
+    calls and as one replay of the graph runner's size-8 graph, back to back
+    with one synchronisation at the end (launch overhead dominates at this
+    size)."""
     from workloads import build_case
     B, L = 8, 512
     wl = build_case(8, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                     prefix_lens=[L - 1] * B, extend_lens=[1] * B, num_pages=4096, device=dev)
     ph = wl.phases[0]
     p = Prepared(wl, ph, dev)
-    g = msgl.DecodeGraph(p.pool, wl.layer, B, wl.num_qo_heads, L, p.pt)
-    g.q.copy_(p.q)
-    g.k.copy_(p.k)
-    g.v.copy_(p.v)
-    g.out_loc.copy_(p.loc)
-    g.table_idx.copy_(p.ti)
-    g.seq_lens.copy_(p.sl)
+    # graphs at 1, 2, 4, 8, 16; the batch of 8 replays the size-8 graph
+    g = msgl.DecodeGraphRunner(p.pool, wl.layer, 16, wl.num_qo_heads, L, p.pt)
+    g.fill(p.q, p.k, p.v, p.loc, p.ti, p.sl, g.pick(B))
 
     def eager():
         run_store(msgl, p)
         run_decode(msgl, p)
 
-    res = {"batch": B, "seq_len": L}
-    for name, fn in (("eager", eager), ("graph", g.launch)):
+    res = {"batch": B, "seq_len": L, "captured_sizes": g.sizes, "replayed_size": g.pick(B)}
+    for name, fn in (("eager", eager), ("graph", lambda: g.launch(B))):
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
@@ -505,7 +502,7 @@ def graph_vs_eager(msgl, dev, iters=300):
             fn()
         torch.cuda.synchronize()
         res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / iters * 1e6, 2)
-    res["graph_matches_eager"] = bool(torch.equal(g.out.view(torch.int16), p.out.view(torch.int16)))
+    res["graph_matches_eager"] = bool(torch.equal(g.out[:B].view(torch.int16), p.out.view(torch.int16)))
     g.close()
 
     # a whole decode step over NL layers (store_kv + decode per layer, the
@@ -553,7 +550,8 @@ def main():
                          "only the step's kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch"],
+    ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch",
+                                       "decode_graph"],
                     help="time only this workload (store_kv + attention) and print its figures; "
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
@@ -574,6 +572,8 @@ def main():
         log(f"{args.only} only")
         if args.only == "mixed_batch":
             res = {"mixed_batch": mixed_stats(msgl, dev, iters=max(1, args.steps))}
+        elif args.only == "decode_graph":
+            res = {"decode_graph": graph_vs_eager(msgl, dev)}
         else:
             res = other_workloads(msgl, dev, ext_iters=max(1, args.steps),
                                   dec_iters=max(1, args.steps), only=args.only)

@@ -314,6 +314,35 @@ msgl_status msgl_decode_graph_launch(const msgl_decode_graph* graph, void* strea
 msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph);
 
 /*
+ * decode_graph_runner: decode graphs at several batch sizes over one set of
+ * static buffers ("Code Notes: mini-sglang", Engine Layer table, GraphRunner
+ * row: graphs for batch sizes 1, 2, 4, 8, ..., and at run time the nearest
+ * captured size at or above the batch).
+ *
+ * create takes the arguments of msgl_decode_graph_create with max_batch
+ * rows in every static buffer and captures one graph per size 1, 2, 4, ...
+ * below max_batch and one at max_batch; each covers the first `size` rows
+ * (the workspace must be sized for max_batch).  pick returns the size a
+ * batch of `batch` rows runs at -- the smallest captured size >= batch --
+ * or 0 when batch is outside 1 .. max_batch; launch replays that graph on
+ * `stream` (MSGL_ERR_SHAPE for a batch outside 1 .. max_batch).  Rows
+ * batch .. size-1 must hold padding (out_loc -1, seq_lens 0, table_idx 0):
+ * the runner reads them as they stand.  Launches of one runner share its
+ * buffers and must be stream-ordered.
+ */
+typedef struct msgl_decode_graph_runner msgl_decode_graph_runner;
+msgl_status msgl_decode_graph_runner_create(
+    const msgl_kv_pool* pool, int32_t layer, const void* k, int64_t k_row_stride, const void* v,
+    int64_t v_row_stride, const int32_t* out_loc, const void* q, int64_t q_row_stride, void* out,
+    const int32_t* page_table, int32_t page_table_stride, const int32_t* table_idx,
+    const int32_t* seq_lens, int32_t max_batch, int32_t num_qo_heads, int32_t max_seq_len,
+    float sm_scale, void* workspace, size_t workspace_bytes, msgl_decode_graph_runner** runner_out);
+int32_t msgl_decode_graph_runner_pick(const msgl_decode_graph_runner* runner, int32_t batch);
+msgl_status msgl_decode_graph_runner_launch(const msgl_decode_graph_runner* runner, int32_t batch,
+                                            void* stream);
+msgl_status msgl_decode_graph_runner_destroy(msgl_decode_graph_runner* runner);
+
+/*
  * paged_mixed: one call for a batch that mixes decode rows and
  * prefill/extend rows, as a scheduler that runs chunked prefill beside
  * decoding builds it ("Code Notes: mini-sglang", Engine Layer table,

@@ -127,6 +127,14 @@ def load_library():
     lib.msgl_decode_graph_launch.argtypes = [P, P]
     lib.msgl_decode_graph_destroy.restype = I32
     lib.msgl_decode_graph_destroy.argtypes = [P]
+    lib.msgl_decode_graph_runner_create.restype = I32
+    lib.msgl_decode_graph_runner_create.argtypes = lib.msgl_decode_graph_create.argtypes
+    lib.msgl_decode_graph_runner_pick.restype = I32
+    lib.msgl_decode_graph_runner_pick.argtypes = [P, I32]
+    lib.msgl_decode_graph_runner_launch.restype = I32
+    lib.msgl_decode_graph_runner_launch.argtypes = [P, I32, P]
+    lib.msgl_decode_graph_runner_destroy.restype = I32
+    lib.msgl_decode_graph_runner_destroy.argtypes = [P]
     _lib = lib
     return lib
 
@@ -394,6 +402,121 @@ def msgl_rope_store_kv(pool: torch.Tensor, layer: int, q: Optional[torch.Tensor]
         _i32(out_loc, "out_loc"), _i32(positions, "positions"), T, cos_sin_table.data_ptr(),
         int(cos_sin_table.shape[0]), _stream(pool))
     _check(st, "msgl_rope_store_kv")
+
+
+class _StaticDecodeBuffers:
+    """The static tensors a captured store_kv + decode reads and writes,
+    for up to `batch` rows, with every row padding (out_loc -1, seq_lens 0,
+    table_idx 0: no store, zero output, no KV read)."""
+
+    def __init__(self, pool: torch.Tensor, batch: int, num_qo_heads: int, max_seq_len: int,
+                 page_table: torch.Tensor, sm_scale: Optional[float]):
+        ps = _pool_struct(pool)
+        if page_table.dim() != 2:
+            raise ValueError("page_table must be 2-D (rows, entries)")
+        dev = pool.device
+        d, hkv = ps.head_dim, ps.num_kv_heads
+        self.batch, self.max_seq_len = int(batch), int(max_seq_len)
+        self.pool, self.page_table = pool, page_table
+        self.q = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
+        self.k = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
+        self.out = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
+        self.out_loc = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+        self.table_idx = torch.zeros((batch,), dtype=torch.int32, device=dev)
+        self.seq_lens = torch.zeros((batch,), dtype=torch.int32, device=dev)
+        need = msgl_paged_decode_workspace_size(batch, num_qo_heads, d, max_seq_len, ps.page_size)
+        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+        self._pool_struct = ps
+        self._args = (ctypes.byref(ps), None, self.k.data_ptr(), hkv * d, self.v.data_ptr(), hkv * d,
+                      self.out_loc.data_ptr(), self.q.data_ptr(), num_qo_heads * d,
+                      self.out.data_ptr(), _i32(page_table, "page_table"), int(page_table.shape[1]),
+                      self.table_idx.data_ptr(), self.seq_lens.data_ptr(), batch, num_qo_heads,
+                      int(max_seq_len), self.sm_scale, self.workspace.data_ptr(),
+                      self.workspace.numel())
+
+    def fill(self, q, k, v, out_loc, table_idx, seq_lens, rows: int) -> int:
+        """Copy a batch of b rows in and make rows b .. rows-1 padding."""
+        b = int(q.shape[0])
+        for name, t, shape in (("q", q, self.q.shape[1:]), ("k", k, self.k.shape[1:]),
+                               ("v", v, self.v.shape[1:])):
+            if t.shape[0] != b or tuple(t.shape[1:]) != tuple(shape) or t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be bf16 shaped ({b}, {tuple(shape)})")
+        for name, t in (("out_loc", out_loc), ("table_idx", table_idx), ("seq_lens", seq_lens)):
+            if t.numel() != b or t.dtype != torch.int32:
+                raise ValueError(f"{name} must be {b} int32 values")
+        self.q[:b].copy_(q)
+        self.k[:b].copy_(k)
+        self.v[:b].copy_(v)
+        self.out_loc[:b].copy_(out_loc)
+        self.table_idx[:b].copy_(table_idx)
+        self.seq_lens[:b].copy_(seq_lens)
+        if b < rows:
+            self.out_loc[b:rows].fill_(-1)
+            self.table_idx[b:rows].fill_(0)
+            self.seq_lens[b:rows].fill_(0)
+        return b
+
+
+class DecodeGraphRunner(_StaticDecodeBuffers):
+    """Decode graphs at batch sizes 1, 2, 4, ... and ``max_batch`` over one
+    set of static buffers (``msgl_decode_graph_runner_*``; "Code Notes:
+    mini-sglang", Engine Layer table, GraphRunner row): a batch of b rows
+    replays the smallest captured size >= b, with rows b .. size-1 padded.
+    ``page_table`` is referenced, not copied."""
+
+    def __init__(self, pool: torch.Tensor, layer: int, max_batch: int, num_qo_heads: int,
+                 max_seq_len: int, page_table: torch.Tensor, sm_scale: Optional[float] = None):
+        super().__init__(pool, max_batch, num_qo_heads, max_seq_len, page_table, sm_scale)
+        args = list(self._args)
+        args[1] = layer
+        handle = ctypes.c_void_p()
+        torch.cuda.synchronize(pool.device)  # the static tensors above are initialised
+        st = load_library().msgl_decode_graph_runner_create(*args, ctypes.byref(handle))
+        _check(st, "msgl_decode_graph_runner_create")
+        self._handle = handle
+        self.sizes = []
+        s = 1
+        while True:
+            self.sizes.append(min(s, self.batch))
+            if self.sizes[-1] == self.batch:
+                break
+            s *= 2
+
+    def pick(self, b: int) -> int:
+        """The captured size a batch of b rows runs at (0 outside 1..max_batch)."""
+        return int(load_library().msgl_decode_graph_runner_pick(self._handle, int(b)))
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out_loc: torch.Tensor,
+            table_idx: torch.Tensor, seq_lens: torch.Tensor) -> torch.Tensor:
+        """Store k/v rows at out_loc and decode q through the picked graph;
+        returns out[:b] (a view of the static output)."""
+        b = int(q.shape[0])
+        size = self.pick(b)
+        if size == 0:
+            raise ValueError(f"batch {b} outside 1..{self.batch}")
+        self.fill(q, k, v, out_loc, table_idx, seq_lens, size)
+        self.launch(b)
+        return self.out[:b]
+
+    def launch(self, b: int) -> None:
+        """Replay the graph for b rows on the current stream over the static
+        buffers as they stand (rows b .. pick(b)-1 must be padding)."""
+        st = load_library().msgl_decode_graph_runner_launch(self._handle, int(b), _stream(self.q))
+        _check(st, "msgl_decode_graph_runner_launch")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            torch.cuda.synchronize(self.q.device)
+            load_library().msgl_decode_graph_runner_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class DecodeGraph:

@@ -102,11 +102,13 @@ int32_t decode_head_group(int32_t num_kv_heads) {
 // int2 per request; then, for each launch of up to kDecodeBatch requests,
 // the fp32 partial outputs of its pieces (pieces, Hq, d) and their
 // (max, sum) pairs.  A launch of b
-// requests splits at most b * max_seq_len tokens over at most kDecodeGrid
-// ranges of >= kDecodeMinTokens, and piece i + r of range i and request r
-// is below ranges + b.
+// requests splits their lengths, each rounded up to whole tiles of at most
+// kDecodeMaxTile tokens (so at most b * (max_seq_len + kDecodeMaxTile - 1)
+// tokens), over at most kDecodeGrid ranges of >= kDecodeMinTokens, and
+// piece i + r of range i and request r is below ranges + b.
 int64_t decode_pieces(int64_t b, int64_t max_seq_len) {
-  const int64_t ranges = std::min<int64_t>(kDecodeGrid, (b * max_seq_len + kDecodeMinTokens - 1) / kDecodeMinTokens);
+  const int64_t tokens = b * (max_seq_len + kDecodeMaxTile - 1);
+  const int64_t ranges = std::min<int64_t>(kDecodeGrid, (tokens + kDecodeMinTokens - 1) / kDecodeMinTokens);
   return ranges + b;
 }
 struct DecodeWorkspace {
@@ -348,6 +350,15 @@ msgl_status scratch_for_current_device(void** ptr) {
 // A captured store_kv + decode: the instantiated HIP graph.
 struct msgl_decode_graph {
   hipGraphExec_t exec;
+};
+
+// Graphs of one set of static buffers at batch sizes 1, 2, 4, ... and the
+// largest size; a launch replays the smallest one that holds the batch.
+constexpr int kMaxRunnerGraphs = 32;
+struct msgl_decode_graph_runner {
+  int32_t count;
+  int32_t sizes[kMaxRunnerGraphs];
+  msgl_decode_graph* graphs[kMaxRunnerGraphs];
 };
 
 extern "C" {
@@ -788,6 +799,66 @@ msgl_status msgl_decode_graph_destroy(msgl_decode_graph* graph) {
   const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
   delete graph;
   return hip_status(e);
+}
+
+msgl_status msgl_decode_graph_runner_destroy(msgl_decode_graph_runner* runner) {
+  if (!runner) return MSGL_OK;
+  msgl_status st = MSGL_OK;
+  for (int32_t i = 0; i < runner->count; ++i) {
+    const msgl_status e = msgl_decode_graph_destroy(runner->graphs[i]);
+    if (st == MSGL_OK) st = e;
+  }
+  delete runner;
+  return st;
+}
+
+msgl_status msgl_decode_graph_runner_create(
+    const msgl_kv_pool* pool, int32_t layer, const void* k, int64_t k_row_stride, const void* v,
+    int64_t v_row_stride, const int32_t* out_loc, const void* q, int64_t q_row_stride, void* out,
+    const int32_t* page_table, int32_t page_table_stride, const int32_t* table_idx,
+    const int32_t* seq_lens, int32_t max_batch, int32_t num_qo_heads, int32_t max_seq_len,
+    float sm_scale, void* workspace, size_t workspace_bytes, msgl_decode_graph_runner** runner_out) {
+  if (!runner_out) return MSGL_ERR_NULL;
+  *runner_out = nullptr;
+  if (max_batch < 1) return MSGL_ERR_SHAPE;
+  msgl_decode_graph_runner* r = new (std::nothrow) msgl_decode_graph_runner;
+  if (!r) return MSGL_ERR_HIP;
+  r->count = 0;
+  for (int64_t s = 1;; s *= 2) {
+    const int32_t size = static_cast<int32_t>(std::min<int64_t>(s, max_batch));
+    msgl_decode_graph* g = nullptr;
+    // each graph covers the first `size` rows of the same static buffers
+    const msgl_status st = msgl_decode_graph_create(
+        pool, layer, k, k_row_stride, v, v_row_stride, out_loc, q, q_row_stride, out, page_table,
+        page_table_stride, table_idx, seq_lens, size, num_qo_heads, max_seq_len, sm_scale,
+        workspace, workspace_bytes, &g);
+    if (st != MSGL_OK) {
+      msgl_decode_graph_runner_destroy(r);
+      return st;
+    }
+    r->sizes[r->count] = size;
+    r->graphs[r->count] = g;
+    ++r->count;
+    if (size == max_batch) break;
+  }
+  *runner_out = r;
+  return MSGL_OK;
+}
+
+int32_t msgl_decode_graph_runner_pick(const msgl_decode_graph_runner* runner, int32_t batch) {
+  if (!runner || batch < 1) return 0;
+  for (int32_t i = 0; i < runner->count; ++i)
+    if (runner->sizes[i] >= batch) return runner->sizes[i];
+  return 0;
+}
+
+msgl_status msgl_decode_graph_runner_launch(const msgl_decode_graph_runner* runner, int32_t batch,
+                                            void* stream) {
+  if (!runner) return MSGL_ERR_NULL;
+  for (int32_t i = 0; i < runner->count; ++i)
+    if (batch >= 1 && runner->sizes[i] >= batch)
+      return msgl_decode_graph_launch(runner->graphs[i], stream);
+  return MSGL_ERR_SHAPE;
 }
 
 }  // extern "C"

@@ -154,7 +154,8 @@ struct GatherParams {
 constexpr int kDecodeGrid = 512;       // workgroups per head group and launch (two per CU)
 constexpr int kDecodeBatch = 2048;     // requests per launch (prefix sums in LDS)
 constexpr int kDecodeWindow = 1024;    // tokens whose slots are staged at once
-constexpr int kDecodeMinTokens = 64;   // tokens per workgroup at least
+constexpr int kDecodeMinTokens = 16;   // tokens per workgroup at least
+constexpr int kDecodeMaxTile = 64;     // tokens per tile at most (lengths are padded to tiles)
 
 struct DecodeParams {
   const uint16_t* k_cache;  // K half of the layer, (slots, Hkv, d)

@@ -65,7 +65,7 @@ constexpr int lds_bytes() {
 template <int D, int RB, int S>
 __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int nwg, int grp,
                                              uint8_t* smem) {
-  constexpr int KB = RB >= 2048 ? 8 : (16384 / RB < 64 ? 16384 / RB : 64);  // tokens per tile
+  constexpr int KB = RB >= 2048 ? 8 : (16384 / RB < kDecodeMaxTile ? 16384 / RB : kDecodeMaxTile);  // tokens per tile
   constexpr int KS = D / 32;                  // k-steps of S^T
   constexpr int CB = D / 16;                  // 16-channel blocks of O^T
   constexpr int NB = KB >= 16 ? KB / 16 : 1;  // 16-key blocks per tile

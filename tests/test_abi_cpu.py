@@ -7,6 +7,8 @@ dereferenced).
 """
 
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -64,12 +66,13 @@ def _pool(**kw):
 def _ws_bytes(batch, hq, d, max_len):
     """A piece map (int2 per request), then per launch of up to 2048
     requests the fp32 partials of its pieces: at most
-    min(512 ranges, ceil(b * max_len / 64)) + b."""
+    min(512 ranges, ceil(b * (max_len + 63) / 16)) + b (lengths are padded
+    to tiles of up to 64 tokens before the split into ranges of >= 16)."""
     a256 = lambda x: -(-x // 256) * 256
     pieces = 0
     for b0 in range(0, batch, 2048):
         b = min(2048, batch - b0)
-        pieces += min(512, -(-b * max_len // 64)) + b
+        pieces += min(512, -(-b * (max_len + 63) // 16)) + b
     return a256(batch * 8) + a256(pieces * hq * d * 4) + pieces * hq * 8
 
 
@@ -79,7 +82,7 @@ def test_workspace_size_is_host_arithmetic():
     f = lib.msgl_paged_decode_workspace_size
     n = f(64, 32, 128, 4096, 16)
     assert n == _ws_bytes(64, 32, 128, 4096)
-    assert f(8, 32, 128, 512, 16) == _ws_bytes(8, 32, 128, 512)  # 72 pieces
+    assert f(8, 32, 128, 512, 16) == _ws_bytes(8, 32, 128, 512)  # 296 pieces
     assert f(3000, 32, 128, 1000, 1) == _ws_bytes(3000, 32, 128, 1000)  # two launches
     assert f(0, 32, 128, 4096, 16) == 0
     assert f(-1, 32, 128, 4096, 16) == 0 and f(4, 32, 128, 4096, 0) == 0
@@ -87,6 +90,47 @@ def test_workspace_size_is_host_arithmetic():
     assert f(64, 32, 128, 4096, 1) == n == f(64, 32, 128, 4096, 13)
     # monotone in batch and length, so one allocation serves smaller calls
     assert f(32, 32, 128, 4096, 16) <= n and f(64, 32, 128, 2048, 16) <= n
+
+
+def _decode_piece_ids(lens, kb):
+    """The piece ids the decode kernel writes for one launch: lengths padded
+    to whole tiles of kb tokens and laid end to end, split into ranges of
+    per = roundup(max(16, ceil(T / 512)), kb) tokens; a request spread over
+    several ranges writes piece i + r from range i."""
+    pad = [-(-max(L, 0) // kb) * kb for L in lens]
+    pre = np.concatenate([[0], np.cumsum(pad)])
+    T = int(pre[-1])
+    per = -(-max(16, -(-T // 512)) // kb) * kb
+    ids = []
+    for r, L in enumerate(lens):
+        if L <= 0:
+            continue
+        first = int(pre[r]) // per
+        pieces = (int(pre[r + 1]) - 1) // per - first + 1
+        if pieces > 1:
+            ids += [first + i + r for i in range(pieces)]
+    return ids
+
+
+def test_workspace_holds_every_piece_the_split_writes():
+    # random and adversarial length mixes (short rows padded to a tile
+    # push the split past batch * max_seq_len tokens), every tile size the
+    # decode kernel uses
+    lib = _lib()
+    f = lib.msgl_paged_decode_workspace_size
+    rng = np.random.default_rng(5)
+    cases = [[17] * 100, [65] * 100, [1] * 300 + [40], [9] * 2048, [4096] * 64, [1]]
+    cases += [list(rng.integers(0, int(rng.integers(1, 3000)), int(rng.integers(1, 400))))
+              for _ in range(200)]
+    for lens in cases:
+        b, max_len = len(lens), max(max(lens), 1)
+        hq, d = 8, 64
+        n = f(b, hq, d, max_len, 16)
+        map_bytes = -(-b * 8 // 256) * 256
+        capacity = (n - map_bytes) // (hq * (d * 4 + 8))  # pieces the partials hold
+        for kb in (8, 16, 32, 64):
+            ids = _decode_piece_ids(lens, kb)
+            assert not ids or max(ids) < capacity, (b, max_len, kb)
 
 
 def test_store_kv_rejects_bad_arguments_without_launch():

@@ -1,5 +1,6 @@
-"""Decode graphs (msgl_decode_graph_*): store_kv + decode captured once at a
-padded batch size and replayed, on gfx950.
+"""Decode graphs (msgl_decode_graph_*, msgl_decode_graph_runner_*):
+store_kv + decode captured once per padded batch size and replayed, on
+gfx950.
 
 Every replay is checked three ways on the same inputs:
   * against the same two calls made eagerly on a copy of the pool:
@@ -88,6 +89,56 @@ def test_decode_graph_replays_match_eager_and_oracle(ps, hq, hkv):
         ok, max_abs, max_rel, rel_l2 = close_report(got, ref, ATOL, RTOL)
         _say(f"replay {it}: max_abs={max_abs:.3e} max_rel={max_rel:.3e} rel_l2={rel_l2:.3e}")
         assert ok and rel_l2 <= REL_L2
+    g.close()
+
+
+@pytest.mark.parametrize("ps,hq,hkv,max_b", [(16, 32, 8, 8), (1, 8, 4, 13)])
+def test_graph_runner_picks_nearest_size_and_matches_oracle(ps, hq, hkv, max_b):
+    # one graph per size 1, 2, 4, ... and max_b; each batch replays the
+    # smallest size >= b and equals the eager calls and the oracle
+    d, cap = 128, 600
+    wl = build_case(340 + ps, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=[cap - 1] * max_b, extend_lens=[1] * max_b)
+    pt = wl.page_table
+    pool = wl.pool.cuda()
+    pt_dev = torch.from_numpy(pt).cuda()
+    _say(f"runner ps={ps} hq={hq} hkv={hkv} max_batch={max_b}")
+    g = msgl.DecodeGraphRunner(pool, 0, max_b, hq, cap, pt_dev)
+    expect = sorted({min(1 << i, max_b) for i in range(8)})
+    assert g.sizes == expect
+    assert g.pick(0) == 0 and g.pick(max_b + 1) == 0
+    for b in range(1, max_b + 1):
+        assert g.pick(b) == min(s for s in expect if s >= b)
+    rng = np.random.default_rng(17 + ps)
+    gen = torch.Generator().manual_seed(19 + ps)
+    for it, b in enumerate([max_b, 5, 1, 3, 2, max_b - 1, 4]):
+        rows = rng.choice(max_b, b, replace=False)
+        table_idx = wl.phases[0].table_idx[rows].astype(np.int32)
+        seq_lens = rng.integers(1, cap + 1, b).astype(np.int32)
+        out_loc = np.array([_slot(pt, table_idx[i], int(seq_lens[i]) - 1, ps) for i in range(b)],
+                           np.int32)
+        q = (torch.randn((b, hq, d), generator=gen)).to(torch.bfloat16)
+        k = (torch.randn((b, hkv, d), generator=gen)).to(torch.bfloat16)
+        v = (torch.randn((b, hkv, d), generator=gen)).to(torch.bfloat16)
+        pool_e = pool.clone()
+        msgl.store_kv(pool_e, 0, k.cuda(), v.cuda(), _i32(out_loc))
+        out_e = msgl.paged_decode(pool_e, 0, q.cuda(), pt_dev, _i32(table_idx), _i32(seq_lens), cap)
+        pool_before = bits(pool)
+        _say(f"runner replay {it}: b={b} size={g.pick(b)}")
+        out_g = g.run(q.cuda(), k.cuda(), v.cuda(), _i32(out_loc), _i32(table_idx),
+                      _i32(seq_lens)).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), "graph != eager"
+        assert torch.equal(pool.view(torch.int16), pool_e.view(torch.int16)), "pool differs"
+        ref_pool = oracle.store_kv(pool_before, 0, bits(k), bits(v), out_loc)
+        ref = oracle.paged_decode(ref_pool, 0, bits(q), pt, table_idx, seq_lens)
+        ok, max_abs, max_rel, rel_l2 = close_report(widen(bits(out_g), np.float64), ref, ATOL, RTOL)
+        _say(f"runner replay {it}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e}")
+        assert ok and rel_l2 <= REL_L2
+    with pytest.raises(ValueError):
+        g.run(*(torch.zeros((max_b + 1,) + t, dtype=torch.bfloat16, device="cuda")
+                for t in ((hq, d), (hkv, d), (hkv, d))),
+              *(torch.zeros(max_b + 1, dtype=torch.int32, device="cuda") for _ in range(3)))
     g.close()
 
 

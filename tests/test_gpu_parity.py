@@ -630,9 +630,8 @@ def test_decode_padding_rows_are_zero():
     assert_close(out, ref, rows=[0, 2], what="decode with a padding row")
 
 
-def test_decode_workspace_reuse_and_split_override(monkeypatch):
-    # a workspace sized for the largest call serves smaller ones; the split
-    # size override changes the partition but not the result
+def test_decode_workspace_reuse():
+    # a workspace sized for the largest call serves smaller ones
     wl = build_case(505, num_qo_heads=16, num_kv_heads=2, head_dim=128, page_size=16,
                     prefix_lens=[1500, 37, 900], extend_lens=[1, 1, 1], kind="decode")
     ph = wl.phases[0]
@@ -642,13 +641,38 @@ def test_decode_workspace_reuse_and_split_override(monkeypatch):
     ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, ph.seq_lens)
     need = msgl.paged_decode_workspace_size(64, 16, 128, 8192, 16)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    for split in ("64", "256", "1024"):
-        monkeypatch.setenv("MSGL_DECODE_SPLIT", split)
-        _say(f"decode split {split}")
+    for rep in range(2):
+        _say(f"decode with an oversized workspace, call {rep}")
         out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
                                 _i32(ph.seq_lens), int(ph.seq_lens.max()), workspace=ws)
         torch.cuda.synchronize()
-        assert_close(out, ref, what=f"decode split {split}")
+        assert_close(out, ref, what=f"decode, reused workspace {rep}")
+
+
+@pytest.mark.parametrize("lens,hkv,d,ps", [([17] * 100, 8, 128, 16), ([65] * 100, 8, 128, 16),
+                                           ([1] * 300 + [40], 4, 128, 1), ([33] * 70, 1, 64, 5)])
+def test_decode_exact_workspace_is_not_overrun(lens, hkv, d, ps):
+    # short requests padded to whole tiles split into more ranges than
+    # batch * max_seq_len / 16: the workspace of exactly the size the
+    # library asks for must hold every piece, and the bytes after it stay
+    # untouched
+    hq = 4 * hkv
+    wl = build_case(507, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=[L - 1 for L in lens], extend_lens=[1] * len(lens), kind="decode")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    max_len = int(ph.seq_lens.max())
+    need = msgl.paged_decode_workspace_size(len(lens), hq, d, max_len, ps)
+    buf = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    _say(f"decode exact workspace B={len(lens)} L={max_len} hkv={hkv} d={d} ps={ps}")
+    out = msgl.paged_decode(dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx),
+                            _i32(ph.seq_lens), max_len, workspace=buf[:need])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "decode wrote past its workspace"
+    pool_bits = oracle.store_kv(bits(wl.pool), 0, bits(ph.k), bits(ph.v), ph.out_loc)
+    ref = oracle.paged_decode(pool_bits, 0, bits(ph.q), wl.page_table, ph.table_idx, ph.seq_lens)
+    assert_close(out, ref, what="decode, exact workspace")
 
 
 # -------------------------------------------------------------- checked mode
