@@ -217,20 +217,45 @@ def rope_store_stats(msgl, p, dev, iters=20):
     q = p.q.clone()
     T, hq, d, hkv = q.shape[0], wl.num_qo_heads, wl.head_dim, wl.num_kv_heads
     nbytes = T * (2 * hq * d * 2 + 2 * 2 * hkv * d * 2 + d * 4 + 8)
-    for _ in range(3):
-        msgl.rope_store_kv(p.pool, wl.layer, q, p.k, p.v, p.loc, posd, table)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for a, b in evs:
-        a.record()
-        msgl.rope_store_kv(p.pool, wl.layer, q, p.k, p.v, p.loc, posd, table)
-        b.record()
-    torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    us = back_to_back_us(lambda: msgl.rope_store_kv(p.pool, wl.layer, q, p.k, p.v, p.loc, posd, table),
+                         iters)
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"rows": T, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
-            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "back-to-back launches between two events"}
+
+
+def back_to_back_us(fn, iters):
+    """Average time per launch of `iters` launches issued back to back
+    between one pair of events: for short kernels, an event pair around each
+    launch would add the host's launch latency to every figure."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+def store_chunk_stats(msgl, dev, iters=50):
+    """store_kv of one 4096-row chunk (the chunked-prefill workload's chunk:
+    32 q / 8 kv heads, d 128, page_size 16), back-to-back launches."""
+    from workloads import build_case
+    wl = build_case(3, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    prefix_lens=[0], extend_lens=[4096], device=dev)
+    ph = wl.phases[0]
+    k, v, loc = ph.k.to(dev), ph.v.to(dev), i32(ph.out_loc, dev)
+    nbytes = 4096 * 2 * 2 * 8 * 128 * 2 + 4096 * 4
+    us = back_to_back_us(lambda: msgl.store_kv(wl.pool, 0, k, v, loc), iters)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del wl
+    return {"rows": 4096, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
+            "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "back-to-back launches between two events"}
 
 
 def alloc_stats(msgl, p, dev, iters=50):
@@ -660,7 +685,7 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    alloc = mixed = rope_stats = graph_stats = others = ceilings = None
+    alloc = mixed = rope_stats = graph_stats = others = ceilings = store_chunk = None
     if not args.step_only:
         log("measured ceilings (copy, read, bf16 GEMM)")
         ceilings = measured_ceilings(dev)
@@ -670,6 +695,8 @@ def main():
         mixed = mixed_stats(msgl, dev)
         log("fused rotary embedding + store_kv (extend rows)")
         rope_stats = rope_store_stats(msgl, pe, dev)
+        log("store_kv of a 4096-row chunk")
+        store_chunk = store_chunk_stats(msgl, dev)
         log("decode graph vs eager calls (small batch)")
         graph_stats = graph_vs_eager(msgl, dev)
         log("chunked 32k prefill and the Qwen3-30B-A3B-geometry decode")
@@ -747,6 +774,7 @@ def main():
             "extend_rows": ph_e.num_tokens,
             "extend_avg_us": round(st_ext_ms * 1e3, 3),
             "extend_GBs": round(sb_ext / (st_ext_ms * 1e-3) / 1e9, 2),
+            "chunk_4096_rows": store_chunk,
         },
         "extend_tflops": round(ext_tflops, 2),
         "decode_graph": graph_stats,

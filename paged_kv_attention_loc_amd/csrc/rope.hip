@@ -23,16 +23,36 @@
 // binary32 with the last bit set when anything was dropped (round to odd),
 // then to nearest even.  The result is the exact rotation of the stored
 // inputs rounded once, up to the fp64 rounding of the sum.
+#include <algorithm>
+
 #include "common.h"
 
 namespace msgl {
 
 namespace {
 
-// a binary64 value rounded to bf16, to nearest, ties to even, in effect in
-// one step (round to odd at binary32 keeps the information the second
-// rounding needs)
+// A binary64 value rounded to bf16, to nearest, ties to even, in effect in
+// one step.  When the result is a normal bf16 (or rounds up to infinity),
+// that is integer work on the binary64 fields: the top 7 of the 52
+// fraction bits are kept, and the 45 below decide the rounding against
+// half a unit (2^44).  Otherwise (zero, results below bf16's normal range,
+// infinities, NaN) the value is rounded to binary32 toward zero with the
+// last bit set when anything was dropped (round to odd), which keeps the
+// information the second rounding, to nearest even, needs.  Both give the
+// correctly rounded result.
 __device__ __forceinline__ uint16_t f64_to_bf16(double y) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, y);
+  const uint32_t hi = static_cast<uint32_t>(bits >> 32);
+  const uint32_t lo = static_cast<uint32_t>(bits);
+  const uint32_t e = (hi >> 20) & 0x7FFu;  // biased binary64 exponent
+  if (e - 897u <= 1150u - 897u) {          // unbiased -126 .. 127
+    const uint32_t m7 = (hi >> 13) & 0x7Fu;
+    const uint32_t rhi = hi & 0x1FFFu;      // top 13 of the 45 dropped bits
+    const bool above = rhi > 0x1000u || (rhi == 0x1000u && lo != 0u);
+    const bool tie = rhi == 0x1000u && lo == 0u;
+    const uint32_t up = (above || (tie && (m7 & 1u))) ? 1u : 0u;
+    return static_cast<uint16_t>(((hi >> 16) & 0x8000u) | ((((e - 896u) << 7) | m7) + up));
+  }
   const float t = __double2float_rz(y);
   const uint32_t u = __float_as_uint(t) | (static_cast<double>(t) != y ? 1u : 0u);
   return f32_to_bf16(__uint_as_float(u));
@@ -66,42 +86,51 @@ __device__ __forceinline__ void rotate8(uint4& x1, uint4& x2, const float* cs, c
 
 }  // namespace
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes read or written once (q, k and v rows stream through)
+__device__ __forceinline__ uint4 load_once(const uint16_t* a) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(a)));
+}
+__device__ __forceinline__ void store_once(uint16_t* a, uint4 x) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, x), reinterpret_cast<u32x4v*>(a));
+}
+
 // Work items per token: Hq*G8 q items and Hkv*G8 k items (G8 = d/16: eight
 // channel pairs each, two 16-byte loads), then Hkv*d/8 v items (one 16-byte
-// piece each).  Consecutive threads take consecutive items of a token.
-__global__ __launch_bounds__(256) void rope_store_kv_kernel(RopeParams p) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+// piece each).  One workgroup per token (blockIdx.x): its slot, position
+// and cos/sin row are workgroup-uniform (scalar loads), and consecutive
+// threads take consecutive items.  The row loads do not wait for the slot:
+// every token has its rows, and only the pool stores depend on the slot.
+__global__ __launch_bounds__(1024) void rope_store_kv_kernel(RopeParams p) {
   const int d = p.head_dim, half = d / 2, g8 = d / 16;
   const int nq = p.num_qo_heads * g8;
   const int nk = p.num_kv_heads * g8;
   const int per_tok = nq + nk + p.num_kv_heads * (d / 8);
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; it < p.num_items;
-       it += stride) {
-    const int64_t t = it / per_tok;
-    const int r = static_cast<int>(it - t * per_tok);
-    const int32_t slot = p.out_loc[t];
-    const bool store = slot >= 0 && slot < p.num_slots;
+  const int64_t t = blockIdx.x;
+  const int32_t slot = p.out_loc[t];
+  const bool store = slot >= 0 && slot < p.num_slots;  // padding rows store nothing
+  const int pos = min(max(p.positions[t], 0), p.max_position - 1);
+  const float* row_cs = p.table + static_cast<int64_t>(pos) * d;
+  for (int r = threadIdx.x; r < per_tok; r += blockDim.x) {
     if (r < nq + nk) {
       const bool is_q = r < nq;
       const int rr = is_q ? r : r - nq;
       const int head = rr / g8, c = rr % g8;
-      const int pos = min(max(p.positions[t], 0), p.max_position - 1);
-      const float* row_cs = p.table + static_cast<int64_t>(pos) * d;
-      if (!is_q && !store) continue;  // padding row: nothing to store
       const uint16_t* src = is_q ? p.q + t * p.q_stride + head * d : p.k + t * p.k_stride + head * d;
-      uint4 x1 = *reinterpret_cast<const uint4*>(src + 8 * c);
-      uint4 x2 = *reinterpret_cast<const uint4*>(src + half + 8 * c);
+      uint4 x1 = load_once(src + 8 * c);
+      uint4 x2 = load_once(src + half + 8 * c);
       rotate8(x1, x2, row_cs + 8 * c, row_cs + half + 8 * c);
+      if (!is_q && !store) continue;
       uint16_t* dst = is_q ? p.q + t * p.q_stride + head * d
                            : p.k_cache + (static_cast<int64_t>(slot) * p.num_kv_heads + head) * d;
-      *reinterpret_cast<uint4*>(dst + 8 * c) = x1;
-      *reinterpret_cast<uint4*>(dst + half + 8 * c) = x2;
+      store_once(dst + 8 * c, x1);
+      store_once(dst + half + 8 * c, x2);
     } else {
-      if (!store) continue;
       const int piece = r - nq - nk;  // 16-byte piece of the v row
-      const uint4 x = *reinterpret_cast<const uint4*>(p.v + t * p.v_stride + 8 * piece);
-      *reinterpret_cast<uint4*>(p.v_cache + static_cast<int64_t>(slot) * p.num_kv_heads * d +
-                                8 * piece) = x;
+      const uint4 x = load_once(p.v + t * p.v_stride + 8 * piece);
+      if (!store) continue;
+      store_once(p.v_cache + static_cast<int64_t>(slot) * p.num_kv_heads * d + 8 * piece, x);
     }
   }
 }
@@ -130,7 +159,13 @@ static int rope_grid(int64_t items) {
 }
 
 hipError_t launch_rope_store_kv(const RopeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(rope_store_kv_kernel, dim3(rope_grid(p.num_items)), dim3(256), 0, stream, p);
+  // one workgroup per token, its items rounded up to whole waves (at most 1024)
+  const int d = p.head_dim;
+  const int per_tok = (p.num_qo_heads + p.num_kv_heads) * (d / 16) + p.num_kv_heads * (d / 8);
+  const int threads = std::min(1024, (per_tok + 63) / 64 * 64);
+  const int64_t tokens = p.num_items / per_tok;
+  hipLaunchKernelGGL(rope_store_kv_kernel, dim3(static_cast<uint32_t>(tokens)), dim3(threads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -38,7 +38,9 @@ struct VecType<2> {
 // rounded up to whole waves, at most 256).  A thread owns one piece position and copies it
 // for the U tokens of its group: the U loads are all issued before the
 // first store, so each thread keeps U independent reads in flight.  The
-// slots are block-uniform (scalar loads).
+// row loads do not wait for the slots (block-uniform scalar loads): every
+// token below num_tokens has a source row, and only the stores depend on
+// the slot.
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   using V = typename VecType<VEC>::T;
@@ -57,8 +59,7 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   for (int u = 0; u < U; ++u) {
     const int64_t t = t0 + u;
     slot[u] = t < p.num_tokens ? p.out_loc[t] : -1;
-    // padding rows (out_loc < 0) and slots outside the pool are skipped
-    if (slot[u] >= 0 && slot[u] < p.num_slots) {
+    if (t < p.num_tokens) {
       if constexpr (VEC == 16) {
         typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
         val[u] = __builtin_bit_cast(V, __builtin_nontemporal_load(
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
       }
     }
   }
+  // padding rows (out_loc < 0) and slots outside the pool are skipped
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (slot[u] >= 0 && slot[u] < p.num_slots) {

@@ -73,6 +73,53 @@ def test_rope_store_kv_bit_exact(hq, hkv, d, ps, merged):
         assert torch.equal(v.cpu().view(torch.int16), v_cpu.view(torch.int16))
 
 
+def test_rope_rounding_ties_overflow_and_tiny_values():
+    # a crafted table and inputs that put the rotated values on the cases of
+    # the rounding to bf16: exact ties at half a unit (even and odd
+    # neighbours), values just above and below a tie, results past bf16's
+    # largest finite value (to infinity), results below its normal range
+    # (subnormal bf16), zeros; compared bit for bit with the oracle
+    hq, hkv, d, ps, T = 4, 1, 64, 16, 64
+    half = d // 2
+    wl = build_case(460, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=[0], extend_lens=[T])
+    ph = wl.phases[0]
+    rng = np.random.default_rng(460)
+    table = np.zeros((4, d), np.float32)
+    table[0, :half] = 1 + 2.0 ** -8                     # cos: x (1 + 2^-8), sin 0
+    table[1, :half] = 0.5
+    table[1, half:] = 2.0 ** -9                         # mixes x1 and x2 at small weight
+    table[2, :half] = np.float32(1 - 2.0 ** -24)
+    table[2, half:] = np.float32(2.0 ** -12)
+    table[3, :half] = 2.0 ** -100                       # pushes results below 2^-126
+    table[3, half:] = 2.0 ** -110
+    specials = np.array([1.0, 1 + 2.0 ** -7, 1 + 3 * 2.0 ** -7, 3.3895313892515355e38,
+                         -3.3895313892515355e38, 2.0 ** -126, -2.0 ** -120, 0.0, 1.5, -1.0,
+                         2.0 ** 100, 3.0e38, 65504.0, 2.0 ** -20], np.float64)
+
+    def make(shape):
+        x = rng.standard_normal(shape) * 2.0 ** rng.integers(-30, 30, shape)
+        x.reshape(-1)[: specials.size * 3] = np.tile(specials, 3)
+        bits16 = oracle.float_to_bf16_bits(x.astype(np.float32))
+        return torch.from_numpy(bits16.view(np.int16)).view(torch.bfloat16)
+
+    q_cpu, k_cpu, v_cpu = make((T, hq, d)), make((T, hkv, d)), make((T, hkv, d))
+    pos = (np.arange(T) % 4).astype(np.int32)
+    pool = wl.pool.cuda()
+    q = q_cpu.cuda()
+    _say("rope rounding cases")
+    msgl.rope_store_kv(pool, 0, q, k_cpu.cuda(), v_cpu.cuda(), _i32(ph.out_loc), _i32(pos),
+                       torch.from_numpy(table).cuda())
+    torch.cuda.synchronize()
+    q_ref, pool_ref = oracle.rope_store_kv(bits(wl.pool), 0, bits(q_cpu), bits(k_cpu), bits(v_cpu),
+                                           ph.out_loc, pos, table)
+    assert np.array_equal(bits(q), q_ref), "rotated q differs"
+    assert np.array_equal(bits(pool), pool_ref), "pool differs"
+    # the crafted rows reach every case: infinities, subnormals and ties
+    qf = oracle.bf16_bits_to_float(q_ref, np.float64)
+    assert np.isinf(qf).any() and ((q_ref & 0x7F80) == 0).any() and (q_ref != 0).any()
+
+
 def test_rope_store_then_decode_matches_oracle():
     # the fused store feeding decode: rotated queries against rotated keys
     hq, hkv, d, ps = 8, 2, 128, 16
