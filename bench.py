@@ -42,23 +42,23 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch from two rocprofv3 --pmc runs of this benchmark
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
 # for a plain 512 MiB device copy (x2 for FETCH_SIZE, x1 for WRITE_SIZE),
-# taken on the kernel sources (and abi.hip, which sets the launch
-# configuration) with these SHA-256 digests.  When a source has changed
-# since, the figure no longer describes the kernel and is reported as null.
+# taken on the kernel sources with these SHA-256 digests.  When a source has
+# changed since, the figure no longer describes the kernel and is reported
+# as null.
 MEASURED_TRAFFIC = {
-    "decode": {  # decode_split_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "b4ae3bce2f7c9085a9e4421b14c33ba5210c44b7ada3523ffe29658e4c019715",
-                    "common.h": "9c4558d3af57e4266079d0fe3027081cb051b1041a710da8726b650c7e2ef2f0",
-                    "abi.hip": "16ac49cce5a726b1f250d845f0ae65dbed6375d98354ad28bd9bed40283c6411"},
-        "bytes": 653306952,
-        "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
+    "decode": {  # decode_kernel + decode_merge_kernel
+        "sources": {"decode.hip": "be0ab79acacfce127b53973a005839af7489e3a661c6d515255e61f39341dce9",
+                    "decode_block.h": "b4d2ad4b51c385cffcab651548a915851f0ab274609f831e625720febff7704d",
+                    "common.h": "e11e4785389f88bcbe3c476b271e69f82d0b2bcac8edd528bed5af174f63f4fe"},
+        "bytes": 658125457,
+        "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {
-        "sources": {"extend.hip": "2bca8344bcd68c94963b5813a7a7a3f789b7b6028378fcc5f29c4e337af488eb",
-                    "common.h": "9c4558d3af57e4266079d0fe3027081cb051b1041a710da8726b650c7e2ef2f0",
-                    "abi.hip": "16ac49cce5a726b1f250d845f0ae65dbed6375d98354ad28bd9bed40283c6411"},
-        "bytes": 239759520,
-        "profile": "profiles/bench_step_llama3-8b-decode_radix-shared-extend.md",
+        "sources": {"extend.hip": "b9efdc8d4ef2287f17972f01a59d0ed1a424c365b70eceec75f5c35d8ff0d091",
+                    "extend_block.h": "3a1bee14ea6361898438a86d15d3cc85a3b7f8474260d84eb4f52cc097f16b4b",
+                    "common.h": "e11e4785389f88bcbe3c476b271e69f82d0b2bcac8edd528bed5af174f63f4fe"},
+        "bytes": 239555029,
+        "profile": "profiles/extend_radix-shared_16x2560.md",
     },
 }
 
@@ -222,23 +222,33 @@ def rope_store_stats(msgl, p, dev, iters=20):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"rows": T, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
             "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "timing": "back-to-back launches between two events"}
+            "timing": "launches back to back in a torch graph, one replay between two events"}
 
 
 def back_to_back_us(fn, iters):
-    """Average time per launch of `iters` launches issued back to back
-    between one pair of events: for short kernels, an event pair around each
-    launch would add the host's launch latency to every figure."""
+    """GPU time per launch of `iters` launches captured back to back in one
+    torch graph, from events around a replay: for short kernels, an event
+    pair around each eager launch would add the host's launch latency, and
+    eager launches back to back would measure the host's launch rate."""
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        fn()
-    b.record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / iters
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / iters)
+    del g
+    return float(np.median(ts))
 
 
 def store_chunk_stats(msgl, dev, iters=50):
@@ -255,7 +265,7 @@ def store_chunk_stats(msgl, dev, iters=50):
     del wl
     return {"rows": 4096, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
             "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "timing": "back-to-back launches between two events"}
+            "timing": "launches back to back in a torch graph, one replay between two events"}
 
 
 def alloc_stats(msgl, p, dev, iters=50):
@@ -576,7 +586,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch",
-                                       "decode_graph"],
+                                       "decode_graph", "rope_store_kv"],
                     help="time only this workload (store_kv + attention) and print its figures; "
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
@@ -599,6 +609,12 @@ def main():
             res = {"mixed_batch": mixed_stats(msgl, dev, iters=max(1, args.steps))}
         elif args.only == "decode_graph":
             res = {"decode_graph": graph_vs_eager(msgl, dev)}
+        elif args.only == "rope_store_kv":
+            from workloads import config_radix_shared_extend
+            wl_ext = config_radix_shared_extend(device=dev)
+            pe = Prepared(wl_ext, wl_ext.phases[0], dev)
+            res = {"rope_store_kv": rope_store_stats(msgl, pe, dev, iters=max(1, args.steps)),
+                   "store_kv_chunk_4096_rows": store_chunk_stats(msgl, dev, iters=max(1, args.steps))}
         else:
             res = other_workloads(msgl, dev, ext_iters=max(1, args.steps),
                                   dec_iters=max(1, args.steps), only=args.only)
