@@ -131,8 +131,8 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int
  *                 valid page ids (entries past that are never read).
  *   table_idx   : (batch,) int32 row indices.
  *   seq_lens    : (batch,) int32 in [0, max_seq_len]; 0 marks a padding row.
- *   max_seq_len : host-side bound used to size the grid and the workspace
- *                 (at most 2048 * 4096 tokens).
+ *   max_seq_len : host-side bound used to size the grid and the workspace;
+ *                 at most 1,048,511 tokens (MSGL_ERR_UNSUPPORTED beyond).
  *   sm_scale    : softmax scale, normally 1/sqrt(head_dim).
  *   workspace   : device buffer, 256-byte aligned, of >=
  *                 msgl_paged_decode_workspace_size(batch, num_qo_heads,

@@ -128,9 +128,10 @@ DecodeWorkspace decode_workspace(int32_t batch, int32_t num_qo_heads, int32_t he
   return w;
 }
 
-// Longest sequence a decode call takes: the token total of a launch fits
-// in int32.
-constexpr int64_t kDecodeMaxSeqLen = (int64_t{1} << 31) / kDecodeBatch - 1;
+// Longest sequence a decode call takes: the token total of a launch, each
+// length padded to whole tiles of up to kDecodeMaxTile tokens, fits in int32.
+constexpr int64_t kDecodeMaxSeqLen = INT32_MAX / kDecodeBatch - kDecodeMaxTile;
+static_assert(kDecodeBatch * (kDecodeMaxSeqLen + kDecodeMaxTile) <= INT32_MAX, "token total");
 
 template <typename T>
 bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {

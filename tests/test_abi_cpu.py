@@ -180,6 +180,15 @@ def test_decode_rejects_bad_arguments_without_launch():
     assert _decode(lib, p, scale=float("nan")) == SHAPE
     # one (K or V, layer) sub-tensor of 2^32 bytes or more
     assert _decode(lib, _pool(num_kv_heads=8, num_pages=1 << 17, page_size=16)) == UNSUP
+    # the longest sequence: 2048 requests of it, each padded to whole tiles
+    # of up to 64 tokens, still sum below 2^31 tokens
+    longest = (2**31 - 1) // 2048 - 64
+    assert 2048 * (longest + 64) < 2**31
+    big_pt = -(-(longest + 1) // 16)
+    assert _decode(lib, p, max_len=longest + 1, pt_stride=big_pt, ws_bytes=1 << 40) == UNSUP
+    # accepted: the call goes on to the workspace check (too small here, so
+    # nothing is launched)
+    assert _decode(lib, p, max_len=longest, pt_stride=big_pt, ws_bytes=16) == WS
 
 
 def test_decode_noalloc_refuses_oversize_without_launch():
