@@ -61,6 +61,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // piece maximum.  One wave per (request, q head): lane l owns float4 piece
 // l % (D/4) of the head and the pieces i = l / (D/4) (mod 64 / (D/4)); the
 // lanes that share a float4 are joined by exchanges 32 (and 16) lanes apart.
+// Every request of the launch has a piece map entry (no pieces when it has
+// no tokens), and the first kMergeRegs pieces of a lane are loaded together,
+// statistics and partial outputs, before the maximum is known: two
+// dependent rounds of global loads instead of four.
+constexpr int kMergeRegs = 8;
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   constexpr int QPH = D / 4;    // float4 pieces per head
@@ -68,28 +74,50 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   const int head = blockIdx.x;
   const int r = blockIdx.y;
   const int lane = threadIdx.x;
-  // requests with no tokens (padding, or the extend rows of a mixed batch)
-  // have no piece map of this call
-  const int L = p.mixed_cu ? (p.mixed_extend[r] == 1 ? p.mixed_prefix[r] + 1 : 0) : p.seq_lens[r];
-  if (L <= 0) return;
   const int2 map = p.ws_map[r];
   const int pieces = map.y;
-  if (pieces <= 1) return;  // written by the decode kernel itself
+  if (pieces <= 1) return;  // no tokens, or written by the decode kernel itself
   const int Hq = p.num_kv_heads * p.group;
   const int64_t u0 = static_cast<int64_t>(map.x) * Hq + head;  // piece i at u0 + i*Hq
   const int c4 = lane % QPH;
   const int ph = lane / QPH;
+  float2 ml[kMergeRegs];
+  float4 ov[kMergeRegs];
+#pragma unroll
+  for (int k = 0; k < kMergeRegs; ++k) {
+    const int i = ph + NPH * k;
+    ml[k] = make_float2(-INFINITY, 0.f);
+    ov[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < pieces) {
+      const int64_t u = u0 + static_cast<int64_t>(i) * Hq;
+      ml[k] = *reinterpret_cast<const float2*>(p.ws_ml + u * 2);
+      ov[k] = reinterpret_cast<const float4*>(p.ws_o + u * D)[c4];
+    }
+  }
   float mx = -INFINITY;
-  for (int i = lane; i < pieces; i += 64) mx = fmaxf(mx, p.ws_ml[(u0 + static_cast<int64_t>(i) * Hq) * 2]);
-  mx = wave_max(mx);
+#pragma unroll
+  for (int k = 0; k < kMergeRegs; ++k) mx = fmaxf(mx, ml[k].x);
+  for (int i = ph + NPH * kMergeRegs; i < pieces; i += NPH)
+    mx = fmaxf(mx, p.ws_ml[(u0 + static_cast<int64_t>(i) * Hq) * 2]);
+#pragma unroll
+  for (int off = 32; off >= QPH; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
   float den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < kMergeRegs; ++k) {
+    const float wgt = fast_exp2(ml[k].x - mx);  // 0 for the pieces a lane does not have
+    den += wgt * ml[k].y;
+    acc.x += wgt * ov[k].x;
+    acc.y += wgt * ov[k].y;
+    acc.z += wgt * ov[k].z;
+    acc.w += wgt * ov[k].w;
+  }
 #pragma unroll 4
-  for (int i = ph; i < pieces; i += NPH) {
+  for (int i = ph + NPH * kMergeRegs; i < pieces; i += NPH) {
     const int64_t u = u0 + static_cast<int64_t>(i) * Hq;
-    const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + u * 2);
-    const float wgt = fast_exp2(ml.x - mx);
-    den += wgt * ml.y;
+    const float2 m2 = *reinterpret_cast<const float2*>(p.ws_ml + u * 2);
+    const float wgt = fast_exp2(m2.x - mx);
+    den += wgt * m2.y;
     const float4 v = reinterpret_cast<const float4*>(p.ws_o + u * D)[c4];
     acc.x += wgt * v.x;
     acc.y += wgt * v.y;

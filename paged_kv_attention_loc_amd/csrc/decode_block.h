@@ -146,10 +146,13 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
   }
   const int T = pre[B];
 
-  // ---- padding rows (seq_len 0): zeros, no KV read
-  if (!p.mixed_cu) {
-    for (int r = wg; r < B; r += nwg) {
-      if (pre[r + 1] == pre[r]) {
+  // ---- rows without tokens: their piece map says so (the merge then reads
+  // nothing else for them); padding rows (seq_len 0) get zeros and no KV
+  // read, while in a mixed batch they are the extend rows, not ours
+  for (int r = wg; r < B; r += nwg) {
+    if (pre[r + 1] == pre[r]) {
+      if (tid == 0) p.ws_map[r] = make_int2(0, 0);
+      if (!p.mixed_cu) {
         uint4* o = reinterpret_cast<uint4*>(p.out + (static_cast<int64_t>(r) * Hq + grp * hg * G) * D);
         for (int i = tid; i < hg * G * D / 8; i += kThreads) o[i] = make_uint4(0, 0, 0, 0);
       }
@@ -238,18 +241,9 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
 
     bf16x8_t qop[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(0.f);
-      if (computes && h < G)
-        qop[ks] = *reinterpret_cast<const bf16x8_t*>(p.q + io_row * p.q_stride +
-                                                     static_cast<int64_t>(g * G + h) * D + ks * 32 + 8 * n);
-    }
-    // the q operands are redefined by an empty asm once their loads are
-    // done: the waitcnt pass would otherwise keep them pending and make the
-    // first MFMA of every tile wait for the DMA in flight
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -265,6 +259,14 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
       // one: valid rows, masked below).  Every wave is done with the slot
       // table and the stages of the previous window.
       __syncthreads();
+      // the request's q rows, in flight together with the window's page
+      // entries
+      if (w0 == sa && computes && h < G) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qop[ks] = *reinterpret_cast<const bf16x8_t*>(p.q + io_row * p.q_stride +
+                                                       static_cast<int64_t>(g * G + h) * D + ks * 32 + 8 * n);
+      }
       {
         const int ps = p.page_size;
         for (int i = tid; i < ntiles * KB; i += kThreads) {
@@ -275,6 +277,12 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
         }
       }
       __syncthreads();
+      // the q operands are redefined by an empty asm once their loads are
+      // done (the barrier waited for them): the waitcnt pass would otherwise
+      // keep them pending and make the first MFMA of every tile wait for the
+      // DMA in flight
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
 
       auto compute = [&](int t, const uint8_t* kt) __attribute__((always_inline)) {
         const uint8_t* vt = kt + KB * RB;
