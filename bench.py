@@ -47,10 +47,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "be0ab79acacfce127b53973a005839af7489e3a661c6d515255e61f39341dce9",
-                    "decode_block.h": "b4d2ad4b51c385cffcab651548a915851f0ab274609f831e625720febff7704d",
+        "sources": {"decode.hip": "bd8f3942659a8d6fd7494e201c5ad1dedabe7b63f1aab4b56d262d25428e9c57",
+                    "decode_block.h": "d6b34b45141a3bce0f12c2007e2ca55d1d03f1fe18dc94adf24dac1038a5277f",
                     "common.h": "e11e4785389f88bcbe3c476b271e69f82d0b2bcac8edd528bed5af174f63f4fe"},
-        "bytes": 658125457,
+        "bytes": 658134448,
         "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {
