@@ -268,10 +268,13 @@ def store_chunk_stats(msgl, dev, iters=50):
             "timing": "launches back to back in a torch graph, one replay between two events"}
 
 
-def alloc_stats(msgl, p, dev, iters=50):
+def alloc_stats(msgl, p, dev, iters=20):
     """msgl_alloc_pages for one phase's new tokens (a copy of its page table,
-    the pool's unused pages as the free list); the free count is reset
-    before each timed launch."""
+    the pool's unused pages as the free list).  GPU time per launch: `iters`
+    launches captured back to back in a torch graph (each takes the next
+    pages of the list), the free count reset before each timed replay;
+    beside it, one eager launch between two events, which adds the host's
+    launch latency."""
     wl, ph = p.wl, p.ph
     pt = p.pt.clone()
     used = np.unique(wl.page_table[wl.page_table >= 0])
@@ -280,18 +283,43 @@ def alloc_stats(msgl, p, dev, iters=50):
     d_nfree = torch.zeros(1, dtype=torch.int32, device=dev)
     d_status = torch.zeros(1, dtype=torch.int32, device=dev)
     out_loc = torch.empty(ph.num_tokens, dtype=torch.int32, device=dev)
-    ts = []
-    for i in range(iters + 3):
+
+    def launch():
+        msgl.alloc_pages(d_free, d_nfree, pt, p.ti, p.pl, p.el, wl.page_size, out_loc, d_status)
+
+    eager = []
+    for i in range(13):
         d_nfree.fill_(len(free))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        msgl.alloc_pages(d_free, d_nfree, pt, p.ti, p.pl, p.el, wl.page_size, out_loc, d_status)
+        launch()
         b.record()
         torch.cuda.synchronize()
         if i >= 3:
-            ts.append(a.elapsed_time(b) * 1e3)
+            eager.append(a.elapsed_time(b) * 1e3)
     assert int(d_status.item()) == 0
-    return {"requests": ph.batch, "new_tokens": ph.num_tokens, "avg_launch_us": round(float(np.mean(ts)), 2)}
+    d_nfree.fill_(len(free))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            launch()
+    ts = []
+    for _ in range(6):
+        d_nfree.fill_(len(free))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        assert int(d_status.item()) == 0, "the free list ran out inside the timed launches"
+        ts.append(a.elapsed_time(b) * 1e3 / iters)
+    del g
+    return {"requests": ph.batch, "new_tokens": ph.num_tokens,
+            "avg_launch_us": round(float(np.median(ts[1:])), 2),
+            "eager_event_us": round(float(np.mean(eager)), 2),
+            "timing": "launches back to back in a torch graph, one replay between two events"}
 
 
 def mixed_stats(msgl, dev, iters=10):
@@ -588,7 +616,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch",
-                                       "decode_graph", "rope_store_kv"],
+                                       "decode_graph", "rope_store_kv", "alloc_pages"],
                     help="time only this workload (store_kv + attention) and print its figures; "
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
@@ -611,6 +639,12 @@ def main():
             res = {"mixed_batch": mixed_stats(msgl, dev, iters=max(1, args.steps))}
         elif args.only == "decode_graph":
             res = {"decode_graph": graph_vs_eager(msgl, dev)}
+        elif args.only == "alloc_pages":
+            wl_dec = config_llama3_8b_decode(device=dev)
+            wl_ext = config_radix_shared_extend(device=dev)
+            res = {"alloc_pages": {
+                "decode_step": alloc_stats(msgl, Prepared(wl_dec, wl_dec.phases[0], dev), dev),
+                "extend_step": alloc_stats(msgl, Prepared(wl_ext, wl_ext.phases[0], dev), dev)}}
         elif args.only == "rope_store_kv":
             from workloads import config_radix_shared_extend
             wl_ext = config_radix_shared_extend(device=dev)

@@ -24,7 +24,10 @@
 // block-wide exclusive scans (wave shuffles, then the wave totals) give
 // each request its first page and first token, the request's thread writes
 // its pages, and all threads then fill the chunk's out_loc entries (a
-// binary search over the token offsets finds each token's request).
+// binary search over the token offsets finds each token's request).  A
+// request's thread reads up to kAllocUnroll free-list entries before it
+// writes them into its row, so that a prefill request's pages cost a few
+// memory round trips rather than one each.
 #include "common.h"
 
 namespace msgl {
@@ -32,6 +35,7 @@ namespace msgl {
 namespace {
 
 constexpr int kAllocThreads = 1024;
+constexpr int kAllocUnroll = 8;  // free-list reads a thread issues before their stores
 
 // exclusive prefix sum of v over the block; returns this thread's
 // exclusive sum and leaves the block total in *total.  Each wave scans its
@@ -132,8 +136,19 @@ __global__ __launch_bounds__(kAllocThreads) void alloc_pages_kernel(AllocParams 
     const int64_t tok0 = block_exclusive_scan(E, scan_buf, &chunk_toks);
     // this request's new pages
     int32_t* prow = p.page_table + static_cast<int64_t>(row) * p.pt_stride;
-    for (int64_t j = 0; j < need; ++j)
-      prow[have + j] = p.free_pages[num_free - 1 - (page_run + page_first + j)];
+    if (need == 1) {
+      prow[have] = p.free_pages[num_free - 1 - (page_run + page_first)];
+    } else {
+      for (int64_t j0 = 0; j0 < need; j0 += kAllocUnroll) {
+        int32_t pg[kAllocUnroll];
+#pragma unroll
+        for (int u = 0; u < kAllocUnroll; ++u)
+          pg[u] = j0 + u < need ? p.free_pages[num_free - 1 - (page_run + page_first + j0 + u)] : 0;
+#pragma unroll
+        for (int u = 0; u < kAllocUnroll; ++u)
+          if (j0 + u < need) prow[have + j0 + u] = pg[u];
+      }
+    }
     tok_first[t] = tok0;
     req_row[t] = row;
     req_pos0[t] = P;
