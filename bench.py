@@ -48,9 +48,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 MEASURED_TRAFFIC = {
     "decode": {  # decode_kernel + decode_merge_kernel
         "sources": {"decode.hip": "bd8f3942659a8d6fd7494e201c5ad1dedabe7b63f1aab4b56d262d25428e9c57",
-                    "decode_block.h": "d6b34b45141a3bce0f12c2007e2ca55d1d03f1fe18dc94adf24dac1038a5277f",
+                    "decode_block.h": "141d373daf85e1308ac8c40677eb20656716dfde3bb2517bc1c9d1984e3f5b0b",
                     "common.h": "e11e4785389f88bcbe3c476b271e69f82d0b2bcac8edd528bed5af174f63f4fe"},
-        "bytes": 658134448,
+        "bytes": 658133096,
         "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {

@@ -757,7 +757,7 @@ msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, co
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MSGL_ERR_HIP;
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);  // the capture error is the one reported
     return MSGL_ERR_HIP;
   }
   // the two calls validate every argument before they launch anything; a
@@ -774,15 +774,17 @@ msgl_status msgl_decode_graph_create(const msgl_kv_pool* pool, int32_t layer, co
     st = hip_status(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
   else if (st == MSGL_OK)
     st = MSGL_ERR_HIP;
-  if (graph) hipGraphDestroy(graph);
-  hipStreamDestroy(cs);
+  // clean-up: a failure here leaves nothing to undo, and the status of the
+  // capture (or of the instantiation) is the one reported
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(cs);
   if (st != MSGL_OK) {
-    if (exec) hipGraphExecDestroy(exec);
+    if (exec) (void)hipGraphExecDestroy(exec);
     return st;
   }
   msgl_decode_graph* g = new (std::nothrow) msgl_decode_graph;
   if (!g) {
-    hipGraphExecDestroy(exec);
+    (void)hipGraphExecDestroy(exec);
     return MSGL_ERR_HIP;
   }
   g->exec = exec;

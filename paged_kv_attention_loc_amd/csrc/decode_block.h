@@ -40,15 +40,15 @@ __device__ __forceinline__ u32x4_t buffer_words(const void* base, uint32_t bytes
 // with an explicit vmcnt before the barrier that publishes the tile.
 // `rs` and `lds_base` are wave-uniform; readfirstlane puts them in SGPRs.
 __device__ __forceinline__ void dma16(u32x4_t rs, const uint8_t* lds_base, uint32_t off) {
-  const uint32_t la = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const uint8_t*)(lds_base))));
+  // the low 32 bits of a generic pointer into LDS are its LDS address
+  const uint32_t la =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
   u32x4_t rsu;
 #pragma unroll
   for (int i = 0; i < 4; ++i) rsu[i] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rs[i]));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :
-               : "s"(la), "v"(off), "s"(rsu)
-               : "memory", "m0");
+  // M0 (the LDS address of the instruction) is an input operand: the
+  // compiler sets it, and knows it holds that value afterwards
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(off), "s"(rsu), "{m0}"(la) : "memory");
 }
 
 
