@@ -42,6 +42,7 @@ __all__ = [
     "paged_extend",
     "debug_gather_kv",
     "DecodeGraph",
+    "DecodeGraphRunner",
     "msgl_rope_store_kv",
     "msgl_rope_cos_sin_table",
     "rope_store_kv",
@@ -436,6 +437,29 @@ class _StaticDecodeBuffers:
                       int(max_seq_len), self.sm_scale, self.workspace.data_ptr(),
                       self.workspace.numel())
 
+    _destroy = None  # the library call that frees the handle
+
+    def _create(self, fn: str, layer: int):
+        """Capture through the library call `fn` over these buffers."""
+        args = list(self._args)
+        args[1] = layer
+        handle = ctypes.c_void_p()
+        torch.cuda.synchronize(self.pool.device)  # the static tensors are initialised
+        _check(getattr(load_library(), fn)(*args, ctypes.byref(handle)), fn)
+        return handle
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            torch.cuda.synchronize(self.q.device)
+            getattr(load_library(), self._destroy)(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
     def fill(self, q, k, v, out_loc, table_idx, seq_lens, rows: int) -> int:
         """Copy a batch of b rows in and make rows b .. rows-1 padding."""
         b = int(q.shape[0])
@@ -466,16 +490,12 @@ class DecodeGraphRunner(_StaticDecodeBuffers):
     replays the smallest captured size >= b, with rows b .. size-1 padded.
     ``page_table`` is referenced, not copied."""
 
+    _destroy = "msgl_decode_graph_runner_destroy"
+
     def __init__(self, pool: torch.Tensor, layer: int, max_batch: int, num_qo_heads: int,
                  max_seq_len: int, page_table: torch.Tensor, sm_scale: Optional[float] = None):
         super().__init__(pool, max_batch, num_qo_heads, max_seq_len, page_table, sm_scale)
-        args = list(self._args)
-        args[1] = layer
-        handle = ctypes.c_void_p()
-        torch.cuda.synchronize(pool.device)  # the static tensors above are initialised
-        st = load_library().msgl_decode_graph_runner_create(*args, ctypes.byref(handle))
-        _check(st, "msgl_decode_graph_runner_create")
-        self._handle = handle
+        self._handle = self._create("msgl_decode_graph_runner_create", layer)
         self.sizes = []
         s = 1
         while True:
@@ -506,20 +526,8 @@ class DecodeGraphRunner(_StaticDecodeBuffers):
         st = load_library().msgl_decode_graph_runner_launch(self._handle, int(b), _stream(self.q))
         _check(st, "msgl_decode_graph_runner_launch")
 
-    def close(self) -> None:
-        if getattr(self, "_handle", None) is not None and self._handle.value:
-            torch.cuda.synchronize(self.q.device)
-            load_library().msgl_decode_graph_runner_destroy(self._handle)
-            self._handle = None
 
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
-
-
-class DecodeGraph:
+class DecodeGraph(_StaticDecodeBuffers):
     """store_kv of one new K/V row per request + paged decode, captured once
     for a fixed padded batch and replayed with a single graph launch
     (``msgl_decode_graph_*``; "Code Notes: mini-sglang", Engine Layer
@@ -533,38 +541,12 @@ class DecodeGraph:
     graph's launches share its buffers, so they are stream-ordered here.
     """
 
+    _destroy = "msgl_decode_graph_destroy"
+
     def __init__(self, pool: torch.Tensor, layer: int, batch: int, num_qo_heads: int,
                  max_seq_len: int, page_table: torch.Tensor, sm_scale: Optional[float] = None):
-        ps = _pool_struct(pool)
-        if page_table.dim() != 2:
-            raise ValueError("page_table must be 2-D (rows, entries)")
-        dev = pool.device
-        d, hkv = ps.head_dim, ps.num_kv_heads
-        self.batch, self.max_seq_len = int(batch), int(max_seq_len)
-        self.pool, self.page_table = pool, page_table
-        self.q = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
-        self.k = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
-        self.v = torch.zeros((batch, hkv, d), dtype=torch.bfloat16, device=dev)
-        self.out = torch.zeros((batch, num_qo_heads, d), dtype=torch.bfloat16, device=dev)
-        self.out_loc = torch.full((batch,), -1, dtype=torch.int32, device=dev)
-        self.table_idx = torch.zeros((batch,), dtype=torch.int32, device=dev)
-        self.seq_lens = torch.zeros((batch,), dtype=torch.int32, device=dev)
-        need = msgl_paged_decode_workspace_size(batch, num_qo_heads, d, max_seq_len, ps.page_size)
-        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-        if sm_scale is None:
-            sm_scale = 1.0 / math.sqrt(d)
-        self._pool_struct = ps
-        handle = ctypes.c_void_p()
-        torch.cuda.synchronize(dev)  # the static tensors above are initialised
-        lib = load_library()
-        st = lib.msgl_decode_graph_create(
-            ctypes.byref(ps), layer, self.k.data_ptr(), hkv * d, self.v.data_ptr(), hkv * d,
-            self.out_loc.data_ptr(), self.q.data_ptr(), num_qo_heads * d, self.out.data_ptr(),
-            _i32(page_table, "page_table"), int(page_table.shape[1]), self.table_idx.data_ptr(),
-            self.seq_lens.data_ptr(), batch, num_qo_heads, int(max_seq_len), float(sm_scale),
-            self.workspace.data_ptr(), self.workspace.numel(), ctypes.byref(handle))
-        _check(st, "msgl_decode_graph_create")
-        self._handle = handle
+        super().__init__(pool, batch, num_qo_heads, max_seq_len, page_table, sm_scale)
+        self._handle = self._create("msgl_decode_graph_create", layer)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out_loc: torch.Tensor,
             table_idx: torch.Tensor, seq_lens: torch.Tensor) -> torch.Tensor:
@@ -573,23 +555,7 @@ class DecodeGraph:
         b = int(q.shape[0])
         if b < 1 or b > self.batch:
             raise ValueError(f"batch {b} outside 1..{self.batch}")
-        for name, t, shape in (("q", q, self.q.shape[1:]), ("k", k, self.k.shape[1:]),
-                               ("v", v, self.v.shape[1:])):
-            if t.shape[0] != b or tuple(t.shape[1:]) != tuple(shape) or t.dtype != torch.bfloat16:
-                raise ValueError(f"{name} must be bf16 shaped ({b}, {tuple(shape)})")
-        for name, t in (("out_loc", out_loc), ("table_idx", table_idx), ("seq_lens", seq_lens)):
-            if t.numel() != b or t.dtype != torch.int32:
-                raise ValueError(f"{name} must be {b} int32 values")
-        self.q[:b].copy_(q)
-        self.k[:b].copy_(k)
-        self.v[:b].copy_(v)
-        self.out_loc[:b].copy_(out_loc)
-        self.table_idx[:b].copy_(table_idx)
-        self.seq_lens[:b].copy_(seq_lens)
-        if b < self.batch:
-            self.out_loc[b:].fill_(-1)
-            self.table_idx[b:].fill_(0)
-            self.seq_lens[b:].fill_(0)
+        self.fill(q, k, v, out_loc, table_idx, seq_lens, self.batch)
         self.launch()
         return self.out[:b]
 
@@ -598,18 +564,6 @@ class DecodeGraph:
         they stand."""
         st = load_library().msgl_decode_graph_launch(self._handle, _stream(self.q))
         _check(st, "msgl_decode_graph_launch")
-
-    def close(self) -> None:
-        if getattr(self, "_handle", None) is not None and self._handle.value:
-            torch.cuda.synchronize(self.q.device)
-            load_library().msgl_decode_graph_destroy(self._handle)
-            self._handle = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
 
 
 # short names

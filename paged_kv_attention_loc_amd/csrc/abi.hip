@@ -180,7 +180,6 @@ DecodeParams decode_params(const msgl_kv_pool* pool, int32_t layer, const void* 
   p.group = num_qo_heads / pool->num_kv_heads;
   p.head_group = decode_head_group(pool->num_kv_heads);
   p.page_size = pool->page_size;
-  p.stages = 2;
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.half_bytes = static_cast<uint32_t>(half_elems(pool) * 2);
   p.max_seq_len = max_seq_len;
@@ -418,11 +417,10 @@ msgl_status msgl_store_kv(const msgl_kv_pool* pool, int32_t layer, const void* k
       if (s >= num_slots(pool)) return MSGL_ERR_RANGE;
       if (s >= 0) live.push_back(s);
     }
-    std::vector<uint8_t> seen(static_cast<size_t>(num_slots(pool)), 0);
-    for (int32_t s : live) {
-      if (seen[s]) return MSGL_ERR_RANGE;
-      seen[s] = 1;
-    }
+    // two rows into one slot: sorted, equal neighbours (host memory of the
+    // step's size, not of the pool's)
+    std::sort(live.begin(), live.end());
+    if (std::adjacent_find(live.begin(), live.end()) != live.end()) return MSGL_ERR_RANGE;
   }
   StoreParams p;
   p.k = static_cast<const uint8_t*>(k);
@@ -660,14 +658,13 @@ msgl_status msgl_rope_store_kv(const msgl_kv_pool* pool, int32_t layer, void* q,
     if (!copy_to_host(loc, out_loc, static_cast<size_t>(num_tokens), cs) ||
         !copy_to_host(pos, positions, static_cast<size_t>(num_tokens), cs))
       return MSGL_ERR_HIP;
-    std::vector<uint8_t> seen(static_cast<size_t>(num_slots(pool)), 0);
+    std::vector<int32_t> live;
     for (int32_t i = 0; i < num_tokens; ++i) {
       if (pos[i] < 0 || pos[i] >= max_position || loc[i] >= num_slots(pool)) return MSGL_ERR_RANGE;
-      if (loc[i] >= 0) {
-        if (seen[loc[i]]) return MSGL_ERR_RANGE;
-        seen[loc[i]] = 1;
-      }
+      if (loc[i] >= 0) live.push_back(loc[i]);
     }
+    std::sort(live.begin(), live.end());  // two rows into one slot
+    if (std::adjacent_find(live.begin(), live.end()) != live.end()) return MSGL_ERR_RANGE;
   }
   RopeParams p;
   p.q = static_cast<uint16_t*>(q);

@@ -179,7 +179,6 @@ struct DecodeParams {
   int32_t group;       // q heads per kv head
   int32_t head_group;  // kv heads per workgroup: a power of two <= 8 dividing num_kv_heads
   int32_t page_size;
-  int32_t stages;      // LDS stages of the K/V pipeline (2-4)
   int32_t max_seq_len;
   int32_t num_slots;
   uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32

@@ -143,3 +143,36 @@ def test_rope_store_then_decode_matches_oracle():
     diff = np.abs(got - ref)
     assert np.all(diff <= 1e-2 + 1e-2 * np.abs(ref))
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 5e-3
+
+
+def test_checked_mode_rejects_bad_rope_metadata(monkeypatch):
+    # MSGL_CHECK=1 copies out_loc and positions to the host first: two rows
+    # into one slot, a slot past the pool and a position past the table are
+    # refused before any launch, and leave q and the pool as they were
+    monkeypatch.setenv("MSGL_CHECK", "1")
+    hq, hkv, d, ps, max_pos = 8, 2, 64, 16, 512
+    wl = build_case(431, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=[0, 40], extend_lens=[20, 12])
+    ph = wl.phases[0]
+    pos = np.arange(ph.num_tokens, dtype=np.int32)
+    table = torch.from_numpy(oracle.rope_table(max_pos, d, 10000.0).astype(np.float32)).cuda()
+    pool = wl.pool.cuda()
+    q, k, v = ph.q.cuda(), ph.k.cuda(), ph.v.cuda()
+    pool0, q0 = pool.clone(), q.clone()
+    dup = ph.out_loc.copy()
+    dup[5] = dup[17]
+    far = ph.out_loc.copy()
+    far[3] = wl.num_slots
+    late = pos.copy()
+    late[7] = max_pos
+    for loc, p in ((dup, pos), (far, pos), (ph.out_loc, late)):
+        with pytest.raises(msgl.MsglError) as e:
+            msgl.rope_store_kv(pool, 0, q, k, v, _i32(loc), _i32(p), table)
+        assert e.value.status == 5
+    torch.cuda.synchronize()
+    assert torch.equal(pool.view(torch.int16), pool0.view(torch.int16))
+    assert torch.equal(q.view(torch.int16), q0.view(torch.int16))
+    padded = ph.out_loc.copy()
+    padded[[2, 9]] = -1  # padding rows may repeat: they write nothing
+    msgl.rope_store_kv(pool, 0, q, k, v, _i32(padded), _i32(pos), table)
+    torch.cuda.synchronize()
