@@ -35,12 +35,12 @@ struct VecType<2> {
 
 // Grid: x = groups of U tokens, y = blocks of blockDim.x pieces of a
 // token's K row followed by its V row (blockDim.x: the two rows' pieces
-// rounded up to whole waves, at most 256).  A thread owns one piece position and copies it
-// for the U tokens of its group: the U loads are all issued before the
-// first store, so each thread keeps U independent reads in flight.  The
-// row loads do not wait for the slots (block-uniform scalar loads): every
-// token below num_tokens has a source row, and only the stores depend on
-// the slot.
+// rounded up to whole waves, at most 256).  A thread owns one piece
+// position and copies it for the U tokens of its group: the U loads are
+// all issued before the first store, so each thread keeps U independent
+// reads in flight.  The row loads do not wait for the slots (block-uniform
+// scalar loads): every token below num_tokens has a source row, and only
+// the stores depend on the slot.
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   using V = typename VecType<VEC>::T;
