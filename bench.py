@@ -47,17 +47,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "bd8f3942659a8d6fd7494e201c5ad1dedabe7b63f1aab4b56d262d25428e9c57",
-                    "decode_block.h": "141d373daf85e1308ac8c40677eb20656716dfde3bb2517bc1c9d1984e3f5b0b",
+        "sources": {"decode.hip": "59d074b52f7854feea0327039ba3c85081b5dbdfd7c8901d2f4b61e0c7e0b6cf",
+                    "decode_block.h": "276d7f34ab08461f5def4333c0093d68aad9c980fc1027bd93da259827e34b59",
                     "common.h": "aa6366b664cd60a2e3e02f6daf7b05b8b129542634a2c2bfc800e2cffe588653"},
-        "bytes": 658133336,
+        "bytes": 658158303,
         "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {
         "sources": {"extend.hip": "b9efdc8d4ef2287f17972f01a59d0ed1a424c365b70eceec75f5c35d8ff0d091",
                     "extend_block.h": "3a1bee14ea6361898438a86d15d3cc85a3b7f8474260d84eb4f52cc097f16b4b",
                     "common.h": "aa6366b664cd60a2e3e02f6daf7b05b8b129542634a2c2bfc800e2cffe588653"},
-        "bytes": 239283935,
+        "bytes": 239301022,
         "profile": "profiles/extend_radix-shared_16x2560.md",
     },
 }

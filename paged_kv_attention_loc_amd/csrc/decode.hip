@@ -64,8 +64,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // Every request of the launch has a piece map entry (no pieces when it has
 // no tokens), and the first kMergeRegs pieces of a lane are loaded together,
 // statistics and partial outputs, before the maximum is known: two
-// dependent rounds of global loads instead of four.
-constexpr int kMergeRegs = 8;
+// dependent rounds of global loads instead of four, for up to
+// kMergeRegs * 64 / (D/4) pieces (32 at head_dim 128: a 512-token request
+// split into 16-token ranges).  Sixteen against eight took a batch of 8
+// such requests from 24 to 22 us per decode call.
+constexpr int kMergeRegs = 16;
 
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {

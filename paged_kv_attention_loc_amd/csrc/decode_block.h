@@ -104,8 +104,12 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
   // caller's contract and is clamped, so that no page_table entry past the
   // row's bound is read.  In a mixed batch only the rows with one new token
   // are decode rows (length prefix + 1); the others have none here.
+  constexpr int RPT = kDecodeBatch / kThreads;  // requests per thread
+  // page_table row indices of the thread's requests, loaded with the
+  // lengths: the row of the workgroup's first request is then known without
+  // another round trip once the range is found
+  int32_t tix[RPT];
   {
-    constexpr int RPT = kDecodeBatch / kThreads;  // requests per thread
     int lens[RPT];
     int run = 0;
 #pragma unroll
@@ -118,6 +122,7 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
         else
           L = min(p.seq_lens[r], p.max_seq_len);
       }
+      tix[j] = r < B ? p.table_idx[r] : 0;
       lens[j] = (max(L, 0) + KB - 1) / KB * KB;  // whole tiles
       run += lens[j];
     }
@@ -217,16 +222,26 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
     }
   };
 
-  for (int r = [&] {
-         // the request holding token a0: the last r with pre[r] <= a0
-         int lo = 0, hi = B;
-         while (hi - lo > 1) {
-           const int mid = (lo + hi) >> 1;
-           if (pre[mid] <= a0) lo = mid; else hi = mid;
-         }
-         return lo;
-       }();
-       r < B && pre[r] < b0; ++r) {
+  // the request holding token a0: the last r with pre[r] <= a0
+  const int r0 = [&] {
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= a0) lo = mid; else hi = mid;
+    }
+    return lo;
+  }();
+  // its page_table row, from the thread that loaded it, through LDS (the
+  // scan totals are not used past the prologue; the first barrier of the
+  // request's first window publishes it)
+  if (tid == r0 / RPT) {
+    int32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+      if (j == r0 % RPT) v = tix[j];
+    wave_tot[0] = v;
+  }
+  for (int r = r0; r < B && pre[r] < b0; ++r) {
     const int first = pre[r] / per;  // the workgroups holding request r
     const int pieces = (pre[r + 1] - 1) / per - first + 1;
     // this piece: tokens [sa, sb) of request r (both whole tiles; tokens past
@@ -251,7 +266,8 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) o[cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    const int32_t* pt = p.page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
+    const int32_t row_later = r == r0 ? 0 : p.table_idx[r];
+    const int32_t* pt = nullptr;
     for (int w0 = sa; w0 < sb; w0 += kDecodeWindow) {
       const int ntok = min(kDecodeWindow, sb - w0);
       const int ntiles = (ntok + KB - 1) / KB;
@@ -259,6 +275,8 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
       // one: valid rows, masked below).  Every wave is done with the slot
       // table and the stages of the previous window.
       __syncthreads();
+      if (w0 == sa)
+        pt = p.page_table + static_cast<int64_t>(r == r0 ? wave_tot[0] : row_later) * p.pt_stride;
       // the request's q rows, in flight together with the window's page
       // entries
       if (w0 == sa && computes && h < G) {
