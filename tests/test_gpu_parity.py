@@ -14,7 +14,6 @@ configuration the benchmark times.  Every output buffer sits between guard
 rows that must come back untouched.
 """
 
-import math
 import sys
 
 import numpy as np

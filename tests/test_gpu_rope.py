@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import paged_kv_attention_loc_amd as msgl
-from tests._util import bits, from_bits
+from tests._util import bits
 from workloads import build_case
 
 pytestmark = pytest.mark.gpu
