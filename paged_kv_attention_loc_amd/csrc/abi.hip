@@ -84,11 +84,35 @@ msgl_status check_attention_geometry(const msgl_kv_pool* pool, int32_t num_qo_he
   return MSGL_OK;
 }
 
-// Waves per extend workgroup (32 query rows each): 8 by default;
-// MSGL_EXTEND_WAVES=4 selects 128-row workgroups.
-int extend_waves() {
+// Compute units of the current device, looked up once per device.
+std::atomic<int> g_cus[kMaxDevices];
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Waves per extend workgroup (32 query rows each).  MSGL_EXTEND_WAVES=4 or
+// 8 forces one.  Otherwise 8 (256-row workgroups), except for a pure extend
+// call whose 256-row tiles -- at least ceil(total * G / 256) per kv head --
+// cannot give every CU a workgroup: there 4 (twice as many 128-row
+// workgroups) measured 13-17% faster (one 512-token request, or the
+// one-kv-head share of a tensor-parallel GPU), while at 256 tiles and more
+// 8 stays 7-13% ahead.  The mixed launch keeps 8: its decode ranges fill the
+// CUs the extend tiles leave.
+int extend_waves(int64_t total_extend_tokens, int32_t G, int32_t num_kv_heads, bool allow_four) {
   const char* v = std::getenv("MSGL_EXTEND_WAVES");
-  return (v && std::atoi(v) == 4) ? 4 : 8;
+  if (v && std::atoi(v) == 4) return 4;
+  if (v && std::atoi(v) == 8) return 8;
+  if (!allow_four) return 8;
+  const int64_t tiles = (total_extend_tokens * G + 255) / 256 * num_kv_heads;
+  return tiles < device_cus() ? 4 : 8;
 }
 
 // kv heads per decode workgroup: the largest power of two <= 8 dividing Hkv
@@ -267,7 +291,7 @@ msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q
                           int32_t total_extend_tokens, int32_t max_extend_len,
                           int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
                           bool* nothing_to_do, int64_t* mtiles_out, int* waves_out,
-                          hipStream_t stream) {
+                          bool allow_four_waves, hipStream_t stream) {
   *nothing_to_do = false;
   msgl_status st = check_pool(pool, layer);
   if (st != MSGL_OK) return st;
@@ -294,7 +318,7 @@ msgl_status extend_checks(const msgl_kv_pool* pool, int32_t layer, const void* q
   const int32_t max_pages = (max_seq_len + pool->page_size - 1) / pool->page_size;
   if (max_pages > page_table_stride) return MSGL_ERR_SHAPE;
   const int32_t G = num_qo_heads / pool->num_kv_heads;
-  const int waves = extend_waves();
+  const int waves = extend_waves(total_extend_tokens, G, pool->num_kv_heads, allow_four_waves);
   *waves_out = waves;
   const int64_t rows_per_tile = 32 * waves;
   const int64_t mtiles = (static_cast<int64_t>(max_extend_len) * G + rows_per_tile - 1) / rows_per_tile;
@@ -531,7 +555,7 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
   msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                  table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
                                  total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
-                                 sm_scale, &nothing, &mtiles, &waves,
+                                 sm_scale, &nothing, &mtiles, &waves, true,
                                  static_cast<hipStream_t>(stream));
   if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;
@@ -556,7 +580,7 @@ msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void
   msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
                                  table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
                                  total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
-                                 sm_scale, &nothing, &mtiles, &waves,
+                                 sm_scale, &nothing, &mtiles, &waves, false,
                                  static_cast<hipStream_t>(stream));
   if (st != MSGL_OK || nothing) return st;
   const int32_t d = pool->head_dim;

@@ -520,6 +520,34 @@ def test_extend_four_wave_workgroups(monkeypatch):
     run_full(wl, "extend 4-wave workgroups")
 
 
+def test_extend_workgroup_size_choice(monkeypatch):
+    # a small extend (64 rows x 1 kv head: fewer 256-row tiles than CUs)
+    # runs 128-row workgroups unless MSGL_EXTEND_WAVES says otherwise; the
+    # rows see the same key tiles in the same order either way, so both
+    # sizes give the same bits, and both match the oracle
+    wl = build_case(704, num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=16,
+                    prefix_lens=[900, 0, 333], extend_lens=[300, 64, 17], kind="extend")
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    q = ph.q.cuda()
+    args = (dev.pool, 0, q, dev.pt, _i32(ph.table_idx), _i32(ph.prefix_lens), _i32(ph.extend_lens),
+            _i32(ph.cu_extend_lens), int(ph.extend_lens.max()), int(ph.seq_lens.max()))
+    outs = {}
+    for wv in ("", "8", "4"):
+        if wv:
+            monkeypatch.setenv("MSGL_EXTEND_WAVES", wv)
+        else:
+            monkeypatch.delenv("MSGL_EXTEND_WAVES", raising=False)
+        _say(f"extend workgroup size choice: MSGL_EXTEND_WAVES={wv or 'unset'}")
+        outs[wv] = msgl.paged_extend(*args)
+        torch.cuda.synchronize()
+    _, ref = oracle_phase(bits(wl.pool), wl, ph, blocked=True)
+    assert_close(outs[""], ref, what="extend, automatic workgroup size")
+    assert torch.equal(outs[""].view(torch.int16), outs["4"].view(torch.int16))
+    assert torch.equal(outs["8"].view(torch.int16), outs["4"].view(torch.int16))
+
+
 @pytest.mark.parametrize("E", [1, 2, 7, 31, 32, 33, 63, 64, 65])
 def test_extend_lengths(E):
     wl = build_case(400 + E, num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16,
