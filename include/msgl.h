@@ -198,6 +198,37 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
                               void* stream);
 
 /*
+ * paged_extend_split: msgl_paged_extend for calls too small to give every
+ * compute unit a workgroup (a short prefill, few requests, or few kv heads
+ * as on a tensor-parallel GPU's share): each row tile's keys are split
+ * into shares, one workgroup each, and a second kernel on the same stream
+ * combines the shares with a log-sum-exp merge (the passages cited for
+ * paged_extend; the split itself is this library's, the pages are silent).
+ * Same arguments and result as msgl_paged_extend, within the attention
+ * tolerance (the shares round to fp32 before the merge), plus:
+ *   workspace : device buffer, 256-byte aligned, of >=
+ *               msgl_paged_extend_workspace_size(pool, total_extend_tokens,
+ *               max_seq_len, num_qo_heads) bytes; no initialisation needed.
+ *               NULL, or a size of 0 from that function (a call large
+ *               enough to fill the device), runs msgl_paged_extend.
+ * The size depends on the current device's compute-unit count and on
+ * MSGL_EXTEND_SPLITS (n forces n shares, 1 to 8), so size the workspace on
+ * the device and in the process that makes the call.  Returns
+ * MSGL_ERR_WORKSPACE for a smaller workspace.  Calls sharing a workspace
+ * must not overlap in time.
+ */
+size_t msgl_paged_extend_workspace_size(const msgl_kv_pool* pool, int32_t total_extend_tokens,
+                                        int32_t max_seq_len, int32_t num_qo_heads);
+msgl_status msgl_paged_extend_split(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                                    int64_t q_row_stride, void* out, const int32_t* page_table,
+                                    int32_t page_table_stride, const int32_t* table_idx,
+                                    const int32_t* prefix_lens, const int32_t* extend_lens,
+                                    const int32_t* cu_extend_lens, int32_t batch,
+                                    int32_t total_extend_tokens, int32_t max_extend_len,
+                                    int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rope_store_kv: rotary position embedding of this step's new rows, fused
  * with store_kv ("Code Structure", section Model Layers, get_rope --
  * rotary position embeddings; "Code Notes: mini-sglang", Engine Layer

@@ -34,6 +34,8 @@ __all__ = [
     "paged_decode_noalloc",
     "paged_decode_noalloc_max_workspace",
     "msgl_paged_extend",
+    "msgl_paged_extend_workspace_size",
+    "paged_extend_workspace_size",
     "msgl_debug_gather_kv",
     "store_kv",
     "paged_decode",
@@ -110,6 +112,11 @@ def load_library():
     lib.msgl_paged_extend.restype = I32
     lib.msgl_paged_extend.argtypes = [PP, I32, P, I64, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
                                       F32, P]
+    lib.msgl_paged_extend_workspace_size.restype = SZ
+    lib.msgl_paged_extend_workspace_size.argtypes = [PP, I32, I32, I32]
+    lib.msgl_paged_extend_split.restype = I32
+    lib.msgl_paged_extend_split.argtypes = [PP, I32, P, I64, P, P, I32, P, P, P, P, I32, I32, I32, I32,
+                                            I32, F32, P, SZ, P]
     lib.msgl_debug_gather_kv.restype = I32
     lib.msgl_debug_gather_kv.argtypes = [PP, I32, P, I32, I32, I32, P, P, P]
     lib.msgl_rope_store_kv.restype = I32
@@ -277,8 +284,13 @@ def msgl_paged_extend(pool: torch.Tensor, layer: int, q: torch.Tensor, page_tabl
                       table_idx: torch.Tensor, prefix_lens: torch.Tensor, extend_lens: torch.Tensor,
                       cu_extend_lens: torch.Tensor, max_extend_len: int, max_seq_len: int,
                       sm_scale: Optional[float] = None,
-                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Causal extend attention: q (sum E, Hq, d) -> out (sum E, Hq, d)."""
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      split: bool = True) -> torch.Tensor:
+    """Causal extend attention: q (sum E, Hq, d) -> out (sum E, Hq, d).
+    A call too small to fill the device splits its keys over more
+    workgroups (msgl_paged_extend_split) when `split` is true: its workspace
+    is `workspace`, or allocated here when that is None."""
     ps = _pool_struct(pool)
     T, hq, d = q.shape
     qs = _rows(q, "q", hq, d)
@@ -291,13 +303,31 @@ def msgl_paged_extend(pool: torch.Tensor, layer: int, q: torch.Tensor, page_tabl
         sm_scale = 1.0 / math.sqrt(d)
     if page_table.dim() != 2:
         raise ValueError("page_table must be 2-D (rows, entries)")
-    st = load_library().msgl_paged_extend(
-        ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
-        int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(prefix_lens, "prefix_lens"),
-        _i32(extend_lens, "extend_lens"), _i32(cu_extend_lens, "cu_extend_lens"), B, T,
-        int(max_extend_len), int(max_seq_len), hq, float(sm_scale), _stream(q))
-    _check(st, "msgl_paged_extend")
+    lib = load_library()
+    args = (ctypes.byref(ps), layer, q.data_ptr(), qs, out.data_ptr(), _i32(page_table, "page_table"),
+            int(page_table.shape[1]), _i32(table_idx, "table_idx"), _i32(prefix_lens, "prefix_lens"),
+            _i32(extend_lens, "extend_lens"), _i32(cu_extend_lens, "cu_extend_lens"), B, T,
+            int(max_extend_len), int(max_seq_len), hq, float(sm_scale))
+    need = int(lib.msgl_paged_extend_workspace_size(ctypes.byref(ps), T, int(max_seq_len), hq)) if split else 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        st = lib.msgl_paged_extend_split(*args, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream(q))
+        _check(st, "msgl_paged_extend_split")
+    else:
+        st = lib.msgl_paged_extend(*args, _stream(q))
+        _check(st, "msgl_paged_extend")
     return out
+
+
+def msgl_paged_extend_workspace_size(pool: torch.Tensor, total_extend_tokens: int, max_seq_len: int,
+                                     num_qo_heads: int) -> int:
+    """Bytes of workspace a key-split extend of these sizes needs on the
+    current device (0: the call fills the device without splitting)."""
+    ps = _pool_struct(pool)
+    return int(load_library().msgl_paged_extend_workspace_size(ctypes.byref(ps), int(total_extend_tokens),
+                                                               int(max_seq_len), int(num_qo_heads)))
 
 
 def msgl_paged_mixed(pool: torch.Tensor, layer: int, q: torch.Tensor, page_table: torch.Tensor,
@@ -576,4 +606,5 @@ paged_decode = msgl_paged_decode
 paged_decode_noalloc = msgl_paged_decode_noalloc
 paged_decode_workspace_size = msgl_paged_decode_workspace_size
 paged_extend = msgl_paged_extend
+paged_extend_workspace_size = msgl_paged_extend_workspace_size
 debug_gather_kv = msgl_debug_gather_kv

@@ -152,6 +152,44 @@ DecodeWorkspace decode_workspace(int32_t batch, int32_t num_qo_heads, int32_t he
   return w;
 }
 
+// Key shares per extend row tile (1: none).  MSGL_EXTEND_SPLITS=n forces n
+// (1 to kExtendMaxSplits).  Otherwise a call whose 256-row tiles -- at
+// least ceil(total * G / 256) per kv head -- are fewer than the CUs takes
+// enough shares for about kExtendSplitFill workgroups per CU, at most
+// kExtendMaxSplits and at most one per kExtendKeysPerSplit keys of the
+// longest row.  Shorter rows do better unsplit, with 128-row workgroups:
+// a share then carries too few key tiles for its partial store and the
+// merge launch (one 512-token piece on a 2048 prefix: 57 us split, 62 us
+// with 128-row workgroups; sixteen such pieces of the one-kv-head share:
+// 72 against 63 us; one 4096-token chunk on 12288 at that share: 155
+// against 353 us).
+constexpr int kExtendMaxSplits = 8;
+constexpr int kExtendSplitFill = 2;
+constexpr int kExtendKeysPerSplit = 2048;
+int extend_splits(int64_t total_extend_tokens, int32_t G, int32_t num_kv_heads,
+                  int32_t max_seq_len) {
+  const char* v = std::getenv("MSGL_EXTEND_SPLITS");
+  if (v && v[0]) return std::min(std::max(std::atoi(v), 1), kExtendMaxSplits);
+  const int64_t tiles = (total_extend_tokens * G + 255) / 256 * num_kv_heads;
+  const int64_t cus = device_cus();
+  if (tiles <= 0 || tiles >= cus) return 1;
+  int64_t sp = (kExtendSplitFill * cus + tiles - 1) / tiles;
+  sp = std::min<int64_t>(sp, kExtendMaxSplits);
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, max_seq_len / kExtendKeysPerSplit));
+  return static_cast<int>(std::max<int64_t>(sp, 1));
+}
+
+// Workspace of a key-split extend: fp32 o (tokens, Hq, shares, d), then
+// (m, l) pairs (tokens, Hq, shares), the first part 256-byte aligned.
+int64_t extend_split_o_bytes(int64_t tokens, int32_t num_qo_heads, int splits, int32_t head_dim) {
+  return align256(tokens * num_qo_heads * splits * head_dim * 4);
+}
+int64_t extend_split_bytes(int64_t tokens, int32_t num_qo_heads, int splits, int32_t head_dim) {
+  if (splits <= 1 || tokens <= 0) return 0;
+  return extend_split_o_bytes(tokens, num_qo_heads, splits, head_dim) +
+         tokens * num_qo_heads * splits * 2 * 4;
+}
+
 // Longest sequence a decode call takes: the token total of a launch, each
 // length padded to whole tiles of up to kDecodeMaxTile tokens, fits in int32.
 constexpr int64_t kDecodeMaxSeqLen = INT32_MAX / kDecodeBatch - kDecodeMaxTile;
@@ -278,6 +316,9 @@ ExtendParams extend_params(const msgl_kv_pool* pool, int32_t layer, const void* 
   p.num_slots = static_cast<int32_t>(num_slots(pool));
   p.scale_log2 = sm_scale * kLog2e;
   p.skip_single = skip_single;
+  p.num_splits = 1;
+  p.ws_o = nullptr;
+  p.ws_ml = nullptr;
   return p;
 }
 
@@ -564,6 +605,64 @@ msgl_status msgl_paged_extend(const msgl_kv_pool* pool, int32_t layer, const voi
                                        cu_extend_lens, num_qo_heads, static_cast<int32_t>(mtiles),
                                        max_extend_len, max_seq_len, sm_scale, 0);
   return hip_status(launch_extend(p, d, batch, waves, static_cast<hipStream_t>(stream)));
+}
+
+size_t msgl_paged_extend_workspace_size(const msgl_kv_pool* pool, int32_t total_extend_tokens,
+                                        int32_t max_seq_len, int32_t num_qo_heads) {
+  if (!pool || pool->num_kv_heads < 1 || num_qo_heads < 1 || num_qo_heads % pool->num_kv_heads != 0 ||
+      total_extend_tokens <= 0 || max_seq_len < 1 || (pool->head_dim != 64 && pool->head_dim != 128))
+    return 0;
+  const int32_t G = num_qo_heads / pool->num_kv_heads;
+  const int sp = extend_splits(total_extend_tokens, G, pool->num_kv_heads, max_seq_len);
+  return static_cast<size_t>(extend_split_bytes(total_extend_tokens, num_qo_heads, sp, pool->head_dim));
+}
+
+msgl_status msgl_paged_extend_split(const msgl_kv_pool* pool, int32_t layer, const void* q,
+                                    int64_t q_row_stride, void* out, const int32_t* page_table,
+                                    int32_t page_table_stride, const int32_t* table_idx,
+                                    const int32_t* prefix_lens, const int32_t* extend_lens,
+                                    const int32_t* cu_extend_lens, int32_t batch,
+                                    int32_t total_extend_tokens, int32_t max_extend_len,
+                                    int32_t max_seq_len, int32_t num_qo_heads, float sm_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t need =
+      msgl_paged_extend_workspace_size(pool, total_extend_tokens, max_seq_len, num_qo_heads);
+  if (need == 0 || !workspace)
+    return msgl_paged_extend(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                             table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
+                             total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
+                             sm_scale, stream);
+  if (workspace_bytes < need) return MSGL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MSGL_ERR_SHAPE;
+  bool nothing = false;
+  int64_t mtiles = 0;
+  int waves = 8;
+  msgl_status st = extend_checks(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                 table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
+                                 total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
+                                 sm_scale, &nothing, &mtiles, &waves, false,
+                                 static_cast<hipStream_t>(stream));
+  if (st != MSGL_OK || nothing) return st;
+  const int32_t d = pool->head_dim;
+  const int32_t G = num_qo_heads / pool->num_kv_heads;
+  const int sp = extend_splits(total_extend_tokens, G, pool->num_kv_heads, max_seq_len);
+  if (waves != 8 || mtiles * sp > 65535)  // a forced workgroup size, or a grid too tall
+    return msgl_paged_extend(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                             table_idx, prefix_lens, extend_lens, cu_extend_lens, batch,
+                             total_extend_tokens, max_extend_len, max_seq_len, num_qo_heads,
+                             sm_scale, stream);
+  ExtendParams p = extend_params(pool, layer, q, q_row_stride, out, page_table, page_table_stride,
+                                 table_idx, prefix_lens, extend_lens, cu_extend_lens, num_qo_heads,
+                                 static_cast<int32_t>(mtiles), max_extend_len, max_seq_len, sm_scale,
+                                 0);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.num_splits = sp;
+  p.ws_o = reinterpret_cast<float*>(base);
+  p.ws_ml = reinterpret_cast<float*>(base + extend_split_o_bytes(total_extend_tokens, num_qo_heads, sp, d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_extend(p, d, batch, 8, s));
+  if (st != MSGL_OK) return st;
+  return hip_status(launch_extend_merge(p, d, total_extend_tokens, s));
 }
 
 msgl_status msgl_paged_mixed(const msgl_kv_pool* pool, int32_t layer, const void* q,

@@ -215,6 +215,14 @@ struct ExtendParams {
   uint32_t half_bytes;  // bytes of one (K or V, layer) sub-tensor, < 2^32
   float scale_log2;
   int32_t skip_single;  // mixed batches: rows with one new token are left to decode
+  // key splits: with num_splits > 1 each (request, kv head, row tile) runs
+  // as num_splits workgroups over shares of its key tiles, each writing
+  // fp32 o / l and (m, l) per (token, q head, share) -- at
+  // (token * Hq + head) * num_splits + share of ws_o (x D) and ws_ml (x 2) --
+  // and the merge kernel combines them into out
+  int32_t num_splits;
+  float* ws_o;
+  float* ws_ml;
 };
 
 struct RopeParams {
@@ -269,6 +277,10 @@ hipError_t launch_mixed(const DecodeParams& pd, const ExtendParams& pe, int head
 // caller sizes p.num_mtiles for it.
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int waves,
                          hipStream_t stream);
+// the combine of the key shares of p.num_splits > 1 into out, for `tokens`
+// token rows
+hipError_t launch_extend_merge(const ExtendParams& p, int head_dim, int64_t tokens,
+                               hipStream_t stream);
 hipError_t launch_rope_store_kv(const RopeParams& p, hipStream_t stream);
 hipError_t launch_alloc_pages(const AllocParams& p, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int32_t max_position, int32_t head_dim, double base,

@@ -54,7 +54,13 @@
 //     per million beyond 1e-2 of exact attention; with fp16 none;
 //   * the running maximum only moves when a row's new maximum exceeds it by
 //     more than 2^8 in exp2 terms, so the O rescale is rare; masking runs
-//     only on tiles that cross a row's causal limit.
+//     only on tiles that cross a row's causal limit;
+//   * a call whose row tiles cannot give every CU a workgroup (a short
+//     prefill, or few kv heads) can split each tile's keys into shares,
+//     one workgroup each (z = tile * shares + share, heaviest tiles
+//     first); the shares write fp32 partial outputs with their softmax
+//     statistics and a second kernel combines them with a log-sum-exp
+//     merge, as the decode does for its token ranges.
 #include "extend_block.h"
 
 namespace msgl {
@@ -65,8 +71,42 @@ template <int D, bool POW2, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void extend_kernel(ExtendParams p,
                                                                const int32_t* __restrict__ page_table) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<D, WAVES>()];
+  const int z = static_cast<int>(blockIdx.z);
   extend_block<D, POW2, WAVES>(p, page_table, blockIdx.x, blockIdx.y,
-                               p.num_mtiles - 1 - static_cast<int>(blockIdx.z), lds);
+                               p.num_mtiles - 1 - z / p.num_splits, lds, z % p.num_splits);
+}
+
+// out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M), over the key
+// shares s of one (token, q head), with M the largest share maximum and o_s
+// already divided by l_s.  Thread: one float4 column of one (token, q head).
+template <int D>
+__global__ __launch_bounds__(256) void extend_merge_kernel(ExtendParams p, int64_t pairs) {
+  constexpr int QPH = D / 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t pair = i / QPH;
+  if (pair >= pairs) return;
+  const int c4 = static_cast<int>(i - pair * QPH);
+  const int S = p.num_splits;
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + pair * S;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, ml[s].x);
+  float den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float2 v = ml[s];
+    const float wgt = v.y > 0.f ? v.y * fast_exp2(v.x - mx) : 0.f;
+    const float4 o = reinterpret_cast<const float4*>(p.ws_o + (pair * S + s) * D)[c4];
+    den += wgt;
+    acc.x += wgt * o.x;
+    acc.y += wgt * o.y;
+    acc.z += wgt * o.z;
+    acc.w += wgt * o.w;
+  }
+  const float inv = 1.f / den;
+  uint2 wv;
+  wv.x = pack_bf16(acc.x * inv, acc.y * inv);
+  wv.y = pack_bf16(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(p.out + pair * D + 4 * c4) = wv;
 }
 
 
@@ -74,7 +114,7 @@ namespace {
 
 template <int D, int WAVES>
 void launch_extend_t(const ExtendParams& p, int batch, hipStream_t stream) {
-  const dim3 grid(p.num_kv_heads, batch, p.num_mtiles);
+  const dim3 grid(p.num_kv_heads, batch, p.num_mtiles * p.num_splits);
   if (p.page_shift >= 0)
     hipLaunchKernelGGL((extend_kernel<D, true, WAVES>), grid, dim3(64 * WAVES), 0, stream, p,
                        p.page_table);
@@ -98,6 +138,18 @@ hipError_t launch_extend(const ExtendParams& p, int head_dim, int batch, int wav
     else
       launch_extend_t<64, 4>(p, batch, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_extend_merge(const ExtendParams& p, int head_dim, int64_t tokens,
+                               hipStream_t stream) {
+  const int64_t pairs = tokens * p.num_kv_heads * p.group;
+  const int64_t threads = pairs * (head_dim / 4);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((extend_merge_kernel<128>), grid, dim3(256), 0, stream, p, pairs);
+  else
+    hipLaunchKernelGGL((extend_merge_kernel<64>), grid, dim3(256), 0, stream, p, pairs);
   return hipGetLastError();
 }
 

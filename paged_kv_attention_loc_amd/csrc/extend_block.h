@@ -95,12 +95,13 @@ constexpr int lds_bytes() {
   return 2 * ExtendShape<D, WAVES>::STAGE;
 }
 
-// Row tile `mt` (32*WAVES packed rows) of request r and kv head g.
+// Row tile `mt` (32*WAVES packed rows) of request r and kv head g; with
+// p.num_splits > 1, share `split` of its key tiles.
 // lds: lds_bytes<D, WAVES>() bytes of LDS, 16-byte aligned.
 template <int D, bool POW2, int WAVES>
 __device__ __forceinline__ void extend_block(const ExtendParams& p,
                                              const int32_t* __restrict__ page_table, int g, int r,
-                                             int mt, uint8_t* lds) {
+                                             int mt, uint8_t* lds, int split = 0) {
   using S = ExtendShape<D, WAVES>;
   constexpr int BM = S::BM, BN = S::BN, KS = S::KS, CB = S::CB;
   constexpr int ROWB = S::ROWB, SPR = S::SPR, K_BYTES = S::K_BYTES, STAGE = S::STAGE;
@@ -149,6 +150,19 @@ __device__ __forceinline__ void extend_block(const ExtendParams& p,
   const int wlim_hi = P + wrow1 / G;
   const int kv_end = P + (min(m0 + BM, M) - 1) / G + 1;
   const int ntiles = (kv_end + BN - 1) / BN;
+  // the key tiles this workgroup walks, [t0, t1): all of them, or one
+  // share of the tiles that every row of the tile sees in full (keys up to
+  // the first row's limit), the last share also taking the tiles that
+  // cross the rows' limits.  A share's first tile is then fully visible to
+  // every row, so each row's running maximum starts finite; a share can be
+  // empty when few tiles are shared.
+  const int nsplit = p.num_splits;
+  int t0 = 0, t1 = ntiles;
+  if (nsplit > 1) {
+    const int nfull = min((P + m0 / G + 1) / BN, ntiles);
+    t0 = split * nfull / nsplit;
+    t1 = split + 1 == nsplit ? ntiles : (split + 1) * nfull / nsplit;
+  }
 
   const int32_t* pt = page_table + static_cast<int64_t>(p.table_idx[r]) * p.pt_stride;
   const int ps = p.page_size;
@@ -213,15 +227,17 @@ __device__ __forceinline__ void extend_block(const ExtendParams& p,
     }
   };
 
-  // prologue: tile 0 in stage 0; tile 1 on its way to stage 1; tile 2's
-  // entries in flight (the barrier's fence waits for the DMA)
-  fetch_entries(0);
-  issue_dma(0, 0);
-  if (ntiles > 1) fetch_entries(1);
-  convert_v(0);
-  __syncthreads();
-  if (ntiles > 1) issue_dma(1, 1);
-  if (ntiles > 2) fetch_entries(2);
+  // prologue: tile t0 in stage 0; tile t0+1 on its way to stage 1; tile
+  // t0+2's entries in flight (the barrier's fence waits for the DMA)
+  if (t1 > t0) {
+    fetch_entries(t0);
+    issue_dma(t0, 0);
+    if (t0 + 1 < t1) fetch_entries(t0 + 1);
+    convert_v(0);
+    __syncthreads();
+    if (t0 + 1 < t1) issue_dma(t0 + 1, 1);
+    if (t0 + 2 < t1) fetch_entries(t0 + 2);
+  }
 
   // the q operands are redefined here by an empty asm: the waitcnt pass
   // would otherwise make the first MFMAs of every tile wait on the tile
@@ -386,14 +402,14 @@ __device__ __forceinline__ void extend_block(const ExtendParams& p,
     // rows turned to fp16 by the waves that loaded them; then tile t+2
     // goes into this stage and tile t+3's page entries go out
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (t + 1 < ntiles) convert_v(ST ^ 1);
+    if (t + 1 < t1) convert_v(ST ^ 1);
     __syncthreads();
-    if (t + 2 < ntiles) issue_dma(t + 2, ST);
-    if (t + 3 < ntiles) fetch_entries(t + 3);
+    if (t + 2 < t1) issue_dma(t + 2, ST);
+    if (t + 3 < t1) fetch_entries(t + 3);
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < t1) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise; the lane holds channels 32cb + 8(e/4) + 4hi + e%4 of
@@ -406,6 +422,27 @@ __device__ __forceinline__ void extend_block(const ExtendParams& p,
   // whatever runs next.  Every wave has passed the loop's last barrier, so
   // the stages are free.
   static_assert(WAVES * 32 * ROWB <= 2 * STAGE, "output staging must fit in the stages");
+  if (nsplit > 1) {
+    // ---- one key share: o / l in fp32 and (m, l) of each of the wave's
+    // rows, for the merge kernel.  The lane holds channels 32cb + 8e4 + 4hi
+    // + 0..3 of its row for e4 = 0..3: one 16-byte store each.  A row that
+    // saw no key (an empty share) gives (-inf, 0) and zeros.
+    const float lt = xor32_sum(l_run);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (wave_rows && mrow < M) {
+      const int64_t u = (static_cast<int64_t>(cu_r + ti) * Hq + g * G + hh) * nsplit + split;
+      float* op = p.ws_o + u * D + 4 * hi;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          *reinterpret_cast<float4*>(op + 32 * cb + 8 * e4) =
+              make_float4(o[cb][4 * e4] * inv, o[cb][4 * e4 + 1] * inv, o[cb][4 * e4 + 2] * inv,
+                          o[cb][4 * e4 + 3] * inv);
+      if (hi == 0) *reinterpret_cast<float2*>(p.ws_ml + u * 2) = make_float2(lt > 0.f ? m_run : -INFINITY, lt);
+    }
+    return;
+  }
   {
     const float inv = 1.f / xor32_sum(l_run);
     uint8_t* ow = lds + w * 32 * ROWB;

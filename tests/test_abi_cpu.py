@@ -133,6 +133,48 @@ def test_workspace_holds_every_piece_the_split_writes():
             assert not ids or max(ids) < capacity, (b, max_len, kb)
 
 
+def _extend_split_bytes(T, hq, hkv, d, max_len, cus=256, forced=None):
+    """Key shares of a small extend and their workspace: shares for about
+    two workgroups per CU when the 256-row tiles (ceil(T * G / 256) per kv
+    head) are fewer than the CUs, at most 8 and one per 256 keys of the
+    longest row per 2048 keys; fp32 o (T, Hq, shares, d), 256-byte aligned,
+    then (m, l)."""
+    G = hq // hkv
+    tiles = -(-T * G // 256) * hkv
+    if forced is not None:
+        sp = min(max(forced, 1), 8)
+    elif tiles >= cus:
+        sp = 1
+    else:
+        sp = max(1, min(-(-2 * cus // tiles), 8, max(1, max_len // 2048)))
+    if sp <= 1:
+        return 0
+    return -(-(T * hq * sp * d * 4) // 256) * 256 + T * hq * sp * 8
+
+
+def test_extend_workspace_size_is_host_arithmetic(monkeypatch):
+    # no GPU here: the library takes 256 compute units
+    lib = _lib()
+    f = lib.msgl_paged_extend_workspace_size
+    monkeypatch.delenv("MSGL_EXTEND_SPLITS", raising=False)
+    for hkv, d, T, max_len, hq in [(1, 128, 8192, 2560, 4), (8, 128, 512, 9216, 32), (2, 64, 591, 701, 8),
+                                   (8, 128, 8192, 2560, 32), (1, 128, 4096, 16384, 4), (8, 128, 100, 100, 32),
+                                   (1, 64, 4096, 8192, 8)]:
+        pool = _pool(num_kv_heads=hkv, head_dim=d)
+        assert f(ctypes.byref(pool), T, max_len, hq) == _extend_split_bytes(T, hq, hkv, d, max_len), \
+            (hkv, d, T, max_len, hq)
+    pool = _pool(num_kv_heads=8, head_dim=128)
+    assert f(ctypes.byref(pool), 8192, 2560, 32) == 0  # 1024 tiles: no split
+    assert f(None, 512, 2560, 32) == 0 and f(ctypes.byref(pool), 0, 2560, 32) == 0
+    assert f(ctypes.byref(pool), 512, 2560, 30) == 0  # Hq not a multiple of Hkv
+    assert f(ctypes.byref(pool), 512, 9216, 32) > 0  # 16 tiles of 64 rows x 8 heads, long rows
+    assert f(ctypes.byref(pool), 512, 2560, 32) == 0  # the same with short rows: unsplit
+    monkeypatch.setenv("MSGL_EXTEND_SPLITS", "3")
+    assert f(ctypes.byref(pool), 8192, 2560, 32) == _extend_split_bytes(8192, 32, 8, 128, 2560, forced=3)
+    monkeypatch.setenv("MSGL_EXTEND_SPLITS", "1")
+    assert f(ctypes.byref(pool), 512, 9216, 32) == 0
+
+
 def test_store_kv_rejects_bad_arguments_without_launch():
     lib = _lib()
     p = _pool()

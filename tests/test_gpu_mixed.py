@@ -49,7 +49,9 @@ def test_mixed_batch_matches_oracle_and_separate_calls(hq, hkv, d, ps):
     max_e, max_l = int(ph.extend_lens.max()), int(ph.seq_lens.max())
     _say(f"mixed hq={hq} hkv={hkv} d={d} ps={ps}")
     out = msgl.paged_mixed(pool, 0, q, pt, ti, pl, el, cu, max_e, max_l)
-    ref_ext = msgl.paged_extend(pool, 0, q, pt, ti, pl, el, cu, max_e, max_l)
+    # the extend rows against the unsplit extend kernel, which the mixed
+    # launch runs
+    ref_ext = msgl.paged_extend(pool, 0, q, pt, ti, pl, el, cu, max_e, max_l, split=False)
     # the decode rows alone, through paged_decode with the same grid bound
     dec = [r for r in range(len(P)) if E[r] == 1]
     rows = [int(ph.cu_extend_lens[r]) for r in dec]
@@ -140,6 +142,6 @@ def test_single_launch_all_extend_rows():
     args = (pool, 0, q, pt, _i32(ph.table_idx), _i32(ph.prefix_lens), _i32(ph.extend_lens),
             _i32(ph.cu_extend_lens), max(E), max(p + e for p, e in zip(P, E)))
     out = msgl.paged_mixed(*args)
-    ref = msgl.paged_extend(*args)
+    ref = msgl.paged_extend(*args, split=False)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -521,10 +521,10 @@ def test_extend_four_wave_workgroups(monkeypatch):
 
 
 def test_extend_workgroup_size_choice(monkeypatch):
-    # a small extend (64 rows x 1 kv head: fewer 256-row tiles than CUs)
-    # runs 128-row workgroups unless MSGL_EXTEND_WAVES says otherwise; the
-    # rows see the same key tiles in the same order either way, so both
-    # sizes give the same bits, and both match the oracle
+    # a small extend (fewer 256-row tiles than CUs) without key splits runs
+    # 128-row workgroups unless MSGL_EXTEND_WAVES says otherwise; the rows
+    # see the same key tiles in the same order either way, so both sizes
+    # give the same bits, and both match the oracle
     wl = build_case(704, num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=16,
                     prefix_lens=[900, 0, 333], extend_lens=[300, 64, 17], kind="extend")
     ph = wl.phases[0]
@@ -540,12 +540,52 @@ def test_extend_workgroup_size_choice(monkeypatch):
         else:
             monkeypatch.delenv("MSGL_EXTEND_WAVES", raising=False)
         _say(f"extend workgroup size choice: MSGL_EXTEND_WAVES={wv or 'unset'}")
-        outs[wv] = msgl.paged_extend(*args)
+        outs[wv] = msgl.paged_extend(*args, split=False)
         torch.cuda.synchronize()
     _, ref = oracle_phase(bits(wl.pool), wl, ph, blocked=True)
     assert_close(outs[""], ref, what="extend, automatic workgroup size")
     assert torch.equal(outs[""].view(torch.int16), outs["4"].view(torch.int16))
     assert torch.equal(outs["8"].view(torch.int16), outs["4"].view(torch.int16))
+
+
+@pytest.mark.parametrize("splits", ["", "2", "3", "8"])
+@pytest.mark.parametrize("hq,hkv,d,ps,P,E", [
+    (4, 1, 128, 16, [6000, 4096], [512, 300]),     # a tensor-parallel share
+    (8, 2, 64, 3, [0, 700, 65], [400, 1, 190]),     # short rows: shares of the first tiles are empty
+    (32, 8, 128, 16, [6000], [260]),               # one request in the full geometry
+    (12, 3, 128, 1, [5000, 64], [90, 64]),          # page size 1, a long prefix
+])
+def test_extend_key_split(monkeypatch, splits, hq, hkv, d, ps, P, E):
+    # calls too small to fill the device split each row tile's keys over
+    # several workgroups (automatically when their rows are long, or
+    # MSGL_EXTEND_SPLITS shares) and merge the shares: every element
+    # against the oracle, the guard rows untouched, and a workspace one byte
+    # short refused
+    if splits:
+        monkeypatch.setenv("MSGL_EXTEND_SPLITS", splits)
+    else:
+        monkeypatch.delenv("MSGL_EXTEND_SPLITS", raising=False)
+    wl = build_case(720 + sum(E), num_qo_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    prefix_lens=P, extend_lens=E, kind="extend", std=2.0)
+    ph = wl.phases[0]
+    dev = Dev(wl)
+    msgl.store_kv(dev.pool, 0, ph.k.cuda(), ph.v.cuda(), _i32(ph.out_loc))
+    T = int(ph.extend_lens.sum())
+    max_len = int(ph.seq_lens.max())
+    need = msgl.paged_extend_workspace_size(dev.pool, T, max_len, hq)
+    assert (need > 0) == (bool(splits) or max_len >= 4096), "the call should split its keys"
+    g = Guarded(T, hq, d)
+    args = (dev.pool, 0, ph.q.cuda(), dev.pt, _i32(ph.table_idx), _i32(ph.prefix_lens),
+            _i32(ph.extend_lens), _i32(ph.cu_extend_lens), int(ph.extend_lens.max()), max_len)
+    _say(f"extend key split shares={splits or 'auto'} hq={hq} hkv={hkv} d={d} ps={ps} P={P} E={E}")
+    msgl.paged_extend(*args, out=g.out, workspace=torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    g.check("extend key split")
+    _, ref = oracle_phase(bits(wl.pool), wl, ph, blocked=True)
+    assert_close(g.out, ref, what=f"extend key split {splits or 'auto'}")
+    if need > 0:
+        with pytest.raises(msgl.MsglError):
+            msgl.paged_extend(*args, workspace=torch.zeros(need - 1, dtype=torch.uint8, device="cuda"))
 
 
 @pytest.mark.parametrize("E", [1, 2, 7, 31, 32, 33, 63, 64, 65])
