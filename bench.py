@@ -48,15 +48,15 @@ MEASURED_TRAFFIC = {
     "decode": {  # decode_kernel + decode_merge_kernel
         "sources": {"decode.hip": "59d074b52f7854feea0327039ba3c85081b5dbdfd7c8901d2f4b61e0c7e0b6cf",
                     "decode_block.h": "276d7f34ab08461f5def4333c0093d68aad9c980fc1027bd93da259827e34b59",
-                    "common.h": "aa6366b664cd60a2e3e02f6daf7b05b8b129542634a2c2bfc800e2cffe588653"},
-        "bytes": 658158303,
+                    "common.h": "271cfffca66ec4cea4a54312e57eda0bf94958123a470de6dfa5800153bb9f74"},
+        "bytes": 658160303,
         "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {
-        "sources": {"extend.hip": "b9efdc8d4ef2287f17972f01a59d0ed1a424c365b70eceec75f5c35d8ff0d091",
-                    "extend_block.h": "3a1bee14ea6361898438a86d15d3cc85a3b7f8474260d84eb4f52cc097f16b4b",
-                    "common.h": "aa6366b664cd60a2e3e02f6daf7b05b8b129542634a2c2bfc800e2cffe588653"},
-        "bytes": 239301022,
+        "sources": {"extend.hip": "af078065bcafd978831e86ea92715ea5ad8165c9cbcbed7127efaaf562e9f37a",
+                    "extend_block.h": "411eb8f5d26cc4d860f0d1a87aed9b4ffc28f48e610ee565b7d335b926f40fb3",
+                    "common.h": "271cfffca66ec4cea4a54312e57eda0bf94958123a470de6dfa5800153bb9f74"},
+        "bytes": 236031695,
         "profile": "profiles/extend_radix-shared_16x2560.md",
     },
 }
