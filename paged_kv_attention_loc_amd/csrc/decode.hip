@@ -49,10 +49,10 @@ namespace msgl {
 
 using namespace decode_impl;
 
-template <int D, int RB, int S>
+template <int D, int RB, int S, int STB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<S>()];
-  decode_block<D, RB, S>(p, blockIdx.x, gridDim.x, blockIdx.y, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<S, STB>()];
+  decode_block<D, RB, S, STB>(p, blockIdx.x, gridDim.x, blockIdx.y, smem);
 }
 
 
@@ -147,21 +147,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
 
 namespace {
 
-template <int D, int S>
-void launch_decode_s(const DecodeParams& p, hipStream_t stream) {
+// The head group's kernel: stages of decode_stage_bytes, two of 32 KiB or
+// four of 16 KiB (the same LDS).
+template <int D, int RB>
+void launch_decode_rb(const DecodeParams& p, hipStream_t stream) {
+  constexpr int STB = decode_stage_bytes<D, RB>();
+  constexpr int S = STB == kStageBytes ? 2 : 4;
   const dim3 grid(kDecodeGrid, p.num_kv_heads / p.head_group);
+  hipLaunchKernelGGL((decode_kernel<D, RB, S, STB>), grid, dim3(kThreads), 0, stream, p);
+}
+
+template <int D>
+void launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   switch (p.head_group) {
     case 8:
-      hipLaunchKernelGGL((decode_kernel<D, 8 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      launch_decode_rb<D, 8 * D * 2>(p, stream);
       break;
     case 4:
-      hipLaunchKernelGGL((decode_kernel<D, 4 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      launch_decode_rb<D, 4 * D * 2>(p, stream);
       break;
     case 2:
-      hipLaunchKernelGGL((decode_kernel<D, 2 * D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      launch_decode_rb<D, 2 * D * 2>(p, stream);
       break;
     default:
-      hipLaunchKernelGGL((decode_kernel<D, D * 2, S>), grid, dim3(kThreads), 0, stream, p);
+      launch_decode_rb<D, D * 2>(p, stream);
       break;
   }
 }
@@ -178,13 +187,13 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t 
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  // two stages: with two 8-wave workgroups per CU (LDS and registers allow
-  // no more), one tile of each is in flight while the other is computed;
-  // measured faster than three or four stages at one workgroup per CU
+  // two workgroups of 8 waves per CU (LDS and registers allow no more);
+  // stages as set in launch_decode_d.  Two 32 KiB stages measured faster
+  // than three or four at one workgroup per CU.
   if (head_dim == 128)
-    launch_decode_s<128, 2>(p, stream);
+    launch_decode_d<128>(p, stream);
   else
-    launch_decode_s<64, 2>(p, stream);
+    launch_decode_d<64>(p, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_merge(p, head_dim, stream);

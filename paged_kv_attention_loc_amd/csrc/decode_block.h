@@ -52,20 +52,35 @@ __device__ __forceinline__ void dma16(u32x4_t rs, const uint8_t* lds_base, uint3
 }
 
 
-// LDS bytes of one workgroup with S stages
-template <int S>
+// Stage size of the decode body for a head group's part of a token row
+// (RB bytes): 16 KiB when the group holds one or two kv heads of 128
+// channels -- short rows, whose workgroups compute on one or two waves, so
+// the stream is latency-bound; four such stages keep three tiles in flight
+// in the LDS of two 32 KiB ones (the one-kv-head share of the Llama-3-8B
+// batch: 23.7 against 26.2 us) -- else 32 KiB (at head_dim 64 the four
+// stages measured 2% slower).  The decode kernel and the mixed kernel both
+// take it, so that both cut a batch's tokens into the same tiles and
+// ranges (and give the same bits).
+template <int D, int RB>
+constexpr int decode_stage_bytes() {
+  return D == 128 && RB <= 2 * D * 2 ? 16384 : kStageBytes;
+}
+
+// LDS bytes of one workgroup with S stages of STB bytes
+template <int S, int STB = kStageBytes>
 constexpr int lds_bytes() {
-  return S * kStageBytes + (kDecodeWindow + kDecodeBatch + 1 + kWaves) * 4;
+  return S * STB + (kDecodeWindow + kDecodeBatch + 1 + kWaves) * 4;
 }
 
 // Workgroup `wg` of `nwg` over the token ranges of kv head group `grp`.
 // RB: bytes of the head group's part of a token row (head_group * D * 2).
-// S: LDS stages (tiles in flight while one is computed: S - 1).
-// smem: lds_bytes<S>() bytes of LDS, 16-byte aligned.
-template <int D, int RB, int S>
+// S: LDS stages (tiles in flight while one is computed: S - 1) of STB
+// bytes each (a K tile and a V tile).
+// smem: lds_bytes<S, STB>() bytes of LDS, 16-byte aligned.
+template <int D, int RB, int S, int STB = kStageBytes>
 __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int nwg, int grp,
                                              uint8_t* smem) {
-  constexpr int KB = RB >= 2048 ? 8 : (16384 / RB < kDecodeMaxTile ? 16384 / RB : kDecodeMaxTile);  // tokens per tile
+  constexpr int KB = RB >= 2048 ? 8 : (STB / 2 / RB < kDecodeMaxTile ? STB / 2 / RB : kDecodeMaxTile);  // tokens per tile
   constexpr int KS = D / 32;                  // k-steps of S^T
   constexpr int CB = D / 16;                  // 16-channel blocks of O^T
   constexpr int NB = KB >= 16 ? KB / 16 : 1;  // 16-key blocks per tile
@@ -77,16 +92,16 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int wg, int 
   // whole 256-byte bank windows: K reads of 16 rows at one column, and the V
   // transpose reads of 8 rows at one 32-byte piece, then hit distinct banks
   constexpr bool SWZ = (RB & 255) == 0;
-  static_assert(IPW * kWaves == NI && KB * RB * 2 <= kStageBytes, "tile shape");
+  static_assert(IPW * kWaves == NI && KB * RB * 2 <= STB, "tile shape");
 
   static_assert(S >= 2 && S <= 4, "stages");
   // LDS: S stages, then the window's slots, the token prefix sums of the
   // requests and the per-wave totals of the scan
   uint8_t* const st0 = smem;
-  uint8_t* const st1 = smem + kStageBytes;
-  uint8_t* const st2 = smem + 2 * kStageBytes;
-  uint8_t* const st3 = smem + 3 * kStageBytes;
-  int32_t* const slot_of = reinterpret_cast<int32_t*>(smem + S * kStageBytes);
+  uint8_t* const st1 = smem + STB;
+  uint8_t* const st2 = smem + 2 * STB;
+  uint8_t* const st3 = smem + 3 * STB;
+  int32_t* const slot_of = reinterpret_cast<int32_t*>(smem + S * STB);
   int32_t* const pre = slot_of + kDecodeWindow;
   int32_t* const wave_tot = pre + kDecodeBatch + 1;
   const int tid = threadIdx.x;

@@ -24,7 +24,9 @@
 //     ranges of the decode rows (kDecodeGrid ranges per kv head group).
 //     The extend body needs ~230 registers a lane, so one 8-wave workgroup
 //     fits a CU; with one decode workgroup per CU, the decode body keeps
-//     three LDS stages (two tiles in flight) instead of two;
+//     three 32 KiB LDS stages (two tiles in flight) instead of two (head
+//     groups of one or two kv heads: four 16 KiB stages, as in the decode
+//     kernel);
 //   * LDS is one buffer that either body uses as its own.
 // When the extend tiles alone fill every CU, the two kinds run one after
 // the other, and the decode part, at one workgroup per CU, takes ~7% longer
@@ -57,7 +59,11 @@ __device__ __forceinline__ int mixed_row_tiles(const ExtendParams& p, int r) {
 template <int D, int RB>
 __global__ __launch_bounds__(kMixedThreads, 2) void mixed_kernel(DecodeParams pd, ExtendParams pe,
                                                                   const int32_t* __restrict__ page_table) {
-  constexpr int SMEM = cmax(decode_impl::lds_bytes<kMixedStages>(), extend_impl::lds_bytes<D, kMixedWaves>());
+  // the decode body cuts tokens into the decode kernel's tiles: 32 KiB
+  // stages, kMixedStages of them, or four of 16 KiB for small head groups
+  constexpr int DSTB = decode_impl::decode_stage_bytes<D, RB>();
+  constexpr int DS = DSTB == decode_impl::kStageBytes ? kMixedStages : 4;
+  constexpr int SMEM = cmax(decode_impl::lds_bytes<DS, DSTB>(), extend_impl::lds_bytes<D, kMixedWaves>());
   static_assert(SMEM >= (kDecodeBatch + 1 + kMixedWaves) * 4, "tile list must fit");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   int32_t* const tiles_pre = reinterpret_cast<int32_t*>(smem);  // (B + 1) prefix sums
@@ -126,8 +132,8 @@ __global__ __launch_bounds__(kMixedThreads, 2) void mixed_kernel(DecodeParams pd
   } else {
     const int64_t db = j - n_ext;
     __syncthreads();
-    decode_impl::decode_block<D, RB, kMixedStages>(pd, static_cast<int>(db % kDecodeGrid), kDecodeGrid,
-                                                   static_cast<int>(db / kDecodeGrid), smem);
+    decode_impl::decode_block<D, RB, DS, DSTB>(pd, static_cast<int>(db % kDecodeGrid), kDecodeGrid,
+                                               static_cast<int>(db / kDecodeGrid), smem);
   }
 }
 
