@@ -46,17 +46,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # as null.
 MEASURED_TRAFFIC = {
     "decode": {  # decode_kernel + decode_merge_kernel
-        "sources": {"decode.hip": "59d074b52f7854feea0327039ba3c85081b5dbdfd7c8901d2f4b61e0c7e0b6cf",
-                    "decode_block.h": "276d7f34ab08461f5def4333c0093d68aad9c980fc1027bd93da259827e34b59",
+        "sources": {"decode.hip": "fbd27d913855bfce9fe4af51697e9f6a3fc51f177b3b110d3193ce6d7d88fe9c",
+                    "decode_block.h": "b9d509ffd8512a1f32625e7aee71e53764368633616a36ed238175582dce0bc8",
                     "common.h": "271cfffca66ec4cea4a54312e57eda0bf94958123a470de6dfa5800153bb9f74"},
-        "bytes": 658160303,
+        "bytes": 658159887,
         "profile": "profiles/decode_llama3-8b-geometry_B64.md",
     },
     "extend": {
         "sources": {"extend.hip": "af078065bcafd978831e86ea92715ea5ad8165c9cbcbed7127efaaf562e9f37a",
                     "extend_block.h": "411eb8f5d26cc4d860f0d1a87aed9b4ffc28f48e610ee565b7d335b926f40fb3",
                     "common.h": "271cfffca66ec4cea4a54312e57eda0bf94958123a470de6dfa5800153bb9f74"},
-        "bytes": 236031695,
+        "bytes": 240399440,
         "profile": "profiles/extend_radix-shared_16x2560.md",
     },
 }
