@@ -136,9 +136,9 @@ def test_workspace_holds_every_piece_the_split_writes():
 def _extend_split_bytes(T, hq, hkv, d, max_len, cus=256, forced=None):
     """Key shares of a small extend and their workspace: shares for about
     two workgroups per CU when the 256-row tiles (ceil(T * G / 256) per kv
-    head) are fewer than the CUs, at most 8 and one per 256 keys of the
-    longest row per 2048 keys; fp32 o (T, Hq, shares, d), 256-byte aligned,
-    then (m, l)."""
+    head) are fewer than the CUs, at most 8 and at most one per 2048 keys of
+    the longest row; fp32 o (T, Hq, shares, d), 256-byte aligned, then
+    (m, l)."""
     G = hq // hkv
     tiles = -(-T * G // 256) * hkv
     if forced is not None:
@@ -248,6 +248,31 @@ def test_decode_noalloc_refuses_oversize_without_launch():
     assert f(None, 0, FAKE, 32 * 128, FAKE, FAKE, 256, FAKE, FAKE, 4, 32, 4096, 0.088, None) == NULL
     assert f(ctypes.byref(p), 0, FAKE, 32 * 128, FAKE, FAKE, 256, FAKE, FAKE, 0, 32, 4096, 0.088,
              None) == OK
+
+
+def _extend_split(lib, pool, ws, ws_bytes, **kw):
+    a = dict(layer=0, q=FAKE, q_stride=32 * 128, out=FAKE, pt=FAKE, pt_stride=256, ti=FAKE,
+             pl=FAKE, el=FAKE, cu=FAKE, batch=2, total=100, max_ext=64, max_len=4096, hq=32,
+             scale=0.088)
+    a.update(kw)
+    return lib.msgl_paged_extend_split(ctypes.byref(pool) if pool is not None else None, a["layer"],
+                                       a["q"], a["q_stride"], a["out"], a["pt"], a["pt_stride"], a["ti"],
+                                       a["pl"], a["el"], a["cu"], a["batch"], a["total"], a["max_ext"],
+                                       a["max_len"], a["hq"], a["scale"], ws, ws_bytes, None)
+
+
+def test_extend_split_checks_its_workspace_without_launch(monkeypatch):
+    # a call small enough to split (16 tiles of 256 rows, 4096-key rows):
+    # the workspace is checked before anything touches the GPU
+    monkeypatch.delenv("MSGL_EXTEND_SPLITS", raising=False)
+    lib = _lib()
+    p = _pool(num_kv_heads=8)
+    need = lib.msgl_paged_extend_workspace_size(ctypes.byref(p), 100, 4096, 32)
+    assert need == _extend_split_bytes(100, 32, 8, 128, 4096) > 0
+    assert _extend_split(lib, p, FAKE, need - 1) == WS
+    assert _extend_split(lib, p, FAKE, 16) == WS
+    assert _extend_split(lib, p, FAKE + 64, need) == SHAPE  # misaligned
+    assert _extend_split(lib, None, FAKE, need) == NULL  # no pool: the plain extend's checks
 
 
 def _extend(lib, pool, **kw):
