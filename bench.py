@@ -620,8 +620,8 @@ def main():
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(attention shards by heads/requests with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(attention shards by heads or requests with no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
