@@ -126,6 +126,10 @@ class Prepared:
         need = msgl.paged_decode_workspace_size(ph.batch, wl.num_qo_heads, wl.head_dim,
                                                 self.max_len, wl.page_size)
         self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        # an extend too small to fill the device splits its keys (its own
+        # workspace); the full-geometry workloads need none
+        need = msgl.paged_extend_workspace_size(wl.pool, ph.num_tokens, self.max_len, wl.num_qo_heads)
+        self.ws_ext = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
 
 def run_store(msgl, p):
@@ -139,7 +143,7 @@ def run_decode(msgl, p):
 
 def run_extend(msgl, p):
     msgl.paged_extend(p.pool, p.wl.layer, p.q, p.pt, p.ti, p.pl, p.el, p.cu, p.max_ext, p.max_len,
-                      out=p.out)
+                      out=p.out, workspace=p.ws_ext)
 
 
 def cpu_baseline(wl_dec, ph_dec, wl_ext, ph_ext, budget_s):
@@ -265,6 +269,53 @@ def store_chunk_stats(msgl, dev, iters=50):
     return {"rows": 4096, "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3),
             "GB/s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "timing": "launches back to back in a torch graph, one replay between two events"}
+
+
+def tp_share_stats(msgl, dev, iters=10):
+    """One GPU's share of Llama-3-8B under 8-way tensor parallelism (4 q /
+    1 kv head per GPU; the lengths, pages and value recipe of the
+    full-geometry workloads): the decode batch, the radix-shared extend and
+    the chunked 32k prefill, whose extend calls split their keys.  GPU time
+    per call: `iters` calls captured back to back in a torch graph.  Not a
+    roofline point: at this share the calls are too small to fill the
+    device."""
+    from workloads import config_chunked_prefill, config_llama3_8b_decode, config_radix_shared_extend
+    res = {"workload": "Llama-3-8B attention at tensor parallelism 8: 4q/1kv d128 ps16 per GPU",
+           "timing": "calls back to back in a torch graph, one replay between two events"}
+    wl = config_llama3_8b_decode(device=dev, num_qo_heads=4, num_kv_heads=1)
+    p = Prepared(wl, wl.phases[0], dev)
+    run_store(msgl, p)
+    nb = decode_bytes(wl, p.ph)
+    us = back_to_back_us(lambda: run_decode(msgl, p), iters)
+    res["decode_B64"] = {"algorithmic_bytes": nb, "us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
+                         "frac_of_hbm_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del p, wl
+    wl = config_radix_shared_extend(device=dev, num_qo_heads=4, num_kv_heads=1)
+    p = Prepared(wl, wl.phases[0], dev)
+    run_store(msgl, p)
+    fl = extend_flops(wl, p.ph)
+    us = back_to_back_us(lambda: run_extend(msgl, p), iters)
+    res["radix_shared_extend"] = {"algorithmic_flops": fl, "us": round(us, 2),
+                                  "TFLOP/s": round(fl / us / 1e6, 1),
+                                  "frac_of_mfma_peak": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del p, wl
+    wl = config_chunked_prefill(device=dev, num_qo_heads=4, num_kv_heads=1)
+    preps = [Prepared(wl, ph, dev) for ph in wl.phases]
+    for p in preps:
+        run_store(msgl, p)
+    torch.cuda.synchronize()
+    chunk_us = [back_to_back_us(lambda p=p: run_extend(msgl, p), max(2, iters // 4)) for p in preps]
+    fl = sum(extend_flops(wl, p.ph) for p in preps)
+    tot = sum(chunk_us)
+    res["chunked_prefill"] = {"algorithmic_flops": fl, "us_per_chunk": [round(x, 1) for x in chunk_us],
+                              "us": round(tot, 1), "TFLOP/s": round(fl / tot / 1e6, 1),
+                              "frac_of_mfma_peak": round(fl / tot / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "key_split": [msgl.paged_extend_workspace_size(wl.pool, p.ph.num_tokens,
+                                                                             p.max_len, 4) > 0
+                                            for p in preps]}
+    del preps, wl
+    torch.cuda.empty_cache()
+    return res
 
 
 def alloc_stats(msgl, p, dev, iters=20):
@@ -615,7 +666,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--only", choices=["chunked_prefill", "qwen3_moe_decode", "mixed_batch",
-                                       "decode_graph", "rope_store_kv", "alloc_pages"],
+                                       "decode_graph", "rope_store_kv", "alloc_pages", "tp_share"],
                     help="time only this workload (store_kv + attention) and print its figures; "
                          "for profiles of the workloads outside the step")
     args = ap.parse_args()
@@ -638,6 +689,8 @@ def main():
             res = {"mixed_batch": mixed_stats(msgl, dev, iters=max(1, args.steps))}
         elif args.only == "decode_graph":
             res = {"decode_graph": graph_vs_eager(msgl, dev)}
+        elif args.only == "tp_share":
+            res = {"tp8_share": tp_share_stats(msgl, dev)}
         elif args.only == "alloc_pages":
             wl_dec = config_llama3_8b_decode(device=dev)
             wl_ext = config_radix_shared_extend(device=dev)
@@ -736,7 +789,7 @@ def main():
     sb_dec = store_bytes(wl_dec, ph_d.num_tokens)
     sb_ext = store_bytes(wl_ext, ph_e.num_tokens)
 
-    alloc = mixed = rope_stats = graph_stats = others = ceilings = store_chunk = None
+    alloc = mixed = rope_stats = graph_stats = others = ceilings = store_chunk = tp_share = None
     if not args.step_only:
         log("measured ceilings (copy, read, bf16 GEMM)")
         ceilings = measured_ceilings(dev)
@@ -752,6 +805,8 @@ def main():
         graph_stats = graph_vs_eager(msgl, dev)
         log("chunked 32k prefill and the Qwen3-30B-A3B-geometry decode")
         others = other_workloads(msgl, dev)
+        log("one GPU's share of Llama-3-8B at tensor parallelism 8")
+        tp_share = tp_share_stats(msgl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -833,6 +888,7 @@ def main():
         "alloc_pages": alloc,
         "mixed_batch": mixed,
         "other_workloads": others,
+        "tp8_share": tp_share,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -155,17 +155,18 @@ DecodeWorkspace decode_workspace(int32_t batch, int32_t num_qo_heads, int32_t he
 // Key shares per extend row tile (1: none).  MSGL_EXTEND_SPLITS=n forces n
 // (1 to kExtendMaxSplits).  Otherwise a call whose 256-row tiles -- at
 // least ceil(total * G / 256) per kv head -- are fewer than the CUs takes
-// enough shares for about kExtendSplitFill workgroups per CU, at most
-// kExtendMaxSplits and at most one per kExtendKeysPerSplit keys of the
-// longest row.  Shorter rows do better unsplit, with 128-row workgroups:
-// a share then carries too few key tiles for its partial store and the
-// merge launch (one 512-token piece on a 2048 prefix: 57 us split, 62 us
-// with 128-row workgroups; sixteen such pieces of the one-kv-head share:
-// 72 against 63 us; one 4096-token chunk on 12288 at that share: 155
-// against 353 us).
+// enough shares for one workgroup per CU, at most kExtendMaxSplits and at
+// most one per kExtendKeysPerSplit keys of the longest row; with fewer
+// than two it runs unsplit (128-row workgroups).  Measured against 2, 4
+// and 8 shares forced, back-to-back calls: one 512-token piece on a 2048
+// prefix (64 tiles) 44 us with 4 shares, 55 with 2, 58 with 8, 62
+// unsplit; one 1024-token piece on 8192 (128 tiles) 161 with 2, 169 with
+// 4, 209 unsplit; one 4096-token chunk on 12288 at 4 q / 1 kv head (64
+// tiles) 143 with 4, 150 with 8, 350 unsplit; a 512-token piece with no
+// prefix 16 us unsplit, 28 with 2; from 256 tiles up, unsplit is best.
 constexpr int kExtendMaxSplits = 8;
-constexpr int kExtendSplitFill = 2;
-constexpr int kExtendKeysPerSplit = 2048;
+constexpr int kExtendSplitFill = 1;
+constexpr int kExtendKeysPerSplit = 512;
 int extend_splits(int64_t total_extend_tokens, int32_t G, int32_t num_kv_heads,
                   int32_t max_seq_len) {
   const char* v = std::getenv("MSGL_EXTEND_SPLITS");

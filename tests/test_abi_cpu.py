@@ -134,10 +134,10 @@ def test_workspace_holds_every_piece_the_split_writes():
 
 
 def _extend_split_bytes(T, hq, hkv, d, max_len, cus=256, forced=None):
-    """Key shares of a small extend and their workspace: shares for about
-    two workgroups per CU when the 256-row tiles (ceil(T * G / 256) per kv
-    head) are fewer than the CUs, at most 8 and at most one per 2048 keys of
-    the longest row; fp32 o (T, Hq, shares, d), 256-byte aligned, then
+    """Key shares of a small extend and their workspace: shares for one
+    workgroup per CU when the 256-row tiles (ceil(T * G / 256) per kv head)
+    are fewer than the CUs, at most 8 and at most one per 512 keys of the
+    longest row; fp32 o (T, Hq, shares, d), 256-byte aligned, then
     (m, l)."""
     G = hq // hkv
     tiles = -(-T * G // 256) * hkv
@@ -146,7 +146,7 @@ def _extend_split_bytes(T, hq, hkv, d, max_len, cus=256, forced=None):
     elif tiles >= cus:
         sp = 1
     else:
-        sp = max(1, min(-(-2 * cus // tiles), 8, max(1, max_len // 2048)))
+        sp = max(1, min(-(-cus // tiles), 8, max(1, max_len // 512)))
     if sp <= 1:
         return 0
     return -(-(T * hq * sp * d * 4) // 256) * 256 + T * hq * sp * 8
@@ -168,7 +168,7 @@ def test_extend_workspace_size_is_host_arithmetic(monkeypatch):
     assert f(None, 512, 2560, 32) == 0 and f(ctypes.byref(pool), 0, 2560, 32) == 0
     assert f(ctypes.byref(pool), 512, 2560, 30) == 0  # Hq not a multiple of Hkv
     assert f(ctypes.byref(pool), 512, 9216, 32) > 0  # 16 tiles of 64 rows x 8 heads, long rows
-    assert f(ctypes.byref(pool), 512, 2560, 32) == 0  # the same with short rows: unsplit
+    assert f(ctypes.byref(pool), 512, 600, 32) == 0  # the same with short rows: unsplit
     monkeypatch.setenv("MSGL_EXTEND_SPLITS", "3")
     assert f(ctypes.byref(pool), 8192, 2560, 32) == _extend_split_bytes(8192, 32, 8, 128, 2560, forced=3)
     monkeypatch.setenv("MSGL_EXTEND_SPLITS", "1")

@@ -254,20 +254,22 @@ def config_tiny(device="cpu", seed: int = 1) -> Workload:
                     [ph0, ph1], note="4q/1kv d64 ps16 pool64 L={17,100,256} + extend 16 on 100")
 
 
-def config_llama3_8b_decode(device="cpu", seed: int = 2, batch: int = 64) -> Workload:
+def config_llama3_8b_decode(device="cpu", seed: int = 2, batch: int = 64, num_qo_heads: int = 32,
+                            num_kv_heads: int = 8) -> Workload:
     """Llama-3-8B attention geometry decode: 32 q / 8 kv heads, head_dim 128,
     page_size 16, 64 requests with total lengths uniform in [512, 4096],
     pages scattered in a pool of 32768 pages, N(0,1); store_kv of the 64 new
-    rows, then decode.
+    rows, then decode.  Other head counts (4 q / 1 kv: one GPU's share under
+    8-way tensor parallelism) keep the same lengths and pages.
 
     rng call order: (1) lengths, (2) page permutation, (3) table_idx.
     """
     rng = np.random.default_rng(seed)
-    Hq, Hkv, d, ps, NP = 32, 8, 128, 16, 32768
+    Hq, Hkv, d, ps, NP = num_qo_heads, num_kv_heads, 128, 16, 32768
     B = batch
     L = rng.integers(512, 4096, B, endpoint=True).astype(np.int32)
     return _decode_from_lengths("llama3_8b_decode", seed, rng, L, Hq, Hkv, d, ps, NP, 1.0, device,
-                                note="32q/8kv d128 ps16 B64 L~U[512,4096] pool 32768 pages")
+                                note=f"{Hq}q/{Hkv}kv d128 ps16 B{B} L~U[512,4096] pool 32768 pages")
 
 
 def config_qwen3_moe_decode(device="cpu", seed: int = 5, batch: int = 256) -> Workload:
@@ -307,16 +309,19 @@ def _decode_from_lengths(name, seed, rng, L, Hq, Hkv, d, ps, NP, std, device, no
 
 
 def config_radix_shared_extend(device="cpu", seed: int = 3, batch: int = 16,
-                               prefix: int = 2048, extend: int = 512) -> Workload:
+                               prefix: int = 2048, extend: int = 512, num_qo_heads: int = 32,
+                               num_kv_heads: int = 8) -> Workload:
     """Radix-shared prefix extend: 32 q / 8 kv heads, head_dim 128,
     page_size 16, pool of 32768 pages; 16 requests whose rows all start with
     the same 128 pages holding a 2048-token prefix, each extending 512 new
     tokens on private pages with a causal mask over prefix + extend; N(0,1).
 
+    Other head counts keep the same pages and lengths.
+
     rng call order: (1) page permutation, (2) table_idx.
     """
     rng = np.random.default_rng(seed)
-    Hq, Hkv, d, ps, NP = 32, 8, 128, 16, 32768
+    Hq, Hkv, d, ps, NP = num_qo_heads, num_kv_heads, 128, 16, 32768
     B = batch
     n_shared, n_own = prefix // ps, extend // ps
     perm = rng.permutation(NP).astype(np.int32)[: n_shared + B * n_own]
@@ -334,19 +339,21 @@ def config_radix_shared_extend(device="cpu", seed: int = 3, batch: int = 16,
     q, k, v = _phase_tensors(gen, B * extend, Hq, Hkv, d, 1.0, device)
     ph = Phase("extend", table_idx, P, E, loc.astype(np.int32), q, k, v)
     return Workload("radix_shared_extend", seed, 1, 0, NP, ps, Hkv, Hq, d, 1.0, page_table,
-                    pool, [ph], note="32q/8kv d128 ps16 B16 shared prefix 2048 + extend 512")
+                    pool, [ph], note=f"{Hq}q/{Hkv}kv d128 ps16 B{B} shared prefix {prefix} + extend {extend}")
 
 
 def config_chunked_prefill(device="cpu", seed: int = 4, total: int = 32768,
-                           chunk: int = 4096) -> Workload:
+                           chunk: int = 4096, num_qo_heads: int = 32, num_kv_heads: int = 8) -> Workload:
     """Chunked prefill of one 32768-token request as 8 extend chunks of 4096
     over the growing prefix: 32 q / 8 kv heads, head_dim 128, page_size 16,
     pool of 32768 pages, values N(0, 0.5^2) (standard deviation 0.5).
 
+    Other head counts keep the same pages and lengths.
+
     rng call order: (1) page permutation, (2) table_idx.
     """
     rng = np.random.default_rng(seed)
-    Hq, Hkv, d, ps, NP, std = 32, 8, 128, 16, 32768, 0.5
+    Hq, Hkv, d, ps, NP, std = num_qo_heads, num_kv_heads, 128, 16, 32768, 0.5
     pages = rng.permutation(NP).astype(np.int32)[: total // ps]
     table_idx = rng.choice(2, 1, replace=False).astype(np.int32)
     page_table = _fill_page_table(2, [pages], table_idx)
@@ -360,7 +367,7 @@ def config_chunked_prefill(device="cpu", seed: int = 4, total: int = 32768,
         q, k, v = _phase_tensors(gen, chunk, Hq, Hkv, d, std, device)
         phases.append(Phase("extend", table_idx.copy(), P, E, loc.astype(np.int32), q, k, v))
     return Workload("chunked_prefill", seed, 1, 0, NP, ps, Hkv, Hq, d, std, page_table, pool,
-                    phases, note="32q/8kv d128 ps16 1x32768 as 8 chunks of 4096, std 0.5")
+                    phases, note=f"{Hq}q/{Hkv}kv d128 ps16 1x{total} as {total // chunk} chunks of {chunk}, std 0.5")
 
 
 CONFIG_BUILDERS = {
