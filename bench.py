@@ -379,7 +379,8 @@ def mixed_stats(msgl, dev, iters=10):
     prefill chunk in flight: its tiles leave most CUs to the decode rows)
     and four (their tiles alone fill every CU).  Each as one paged_mixed
     call (one attention launch), as a decode call plus an extend call over
-    the same rows, and as a paged_mixed call made of those same launches
+    the same rows (the extend with its keys split where it takes them, and
+    unsplit), and as a paged_mixed call made of those same launches
     (MSGL_MIXED_SPLIT=1)."""
     res = {}
     for name, n_chunks in (("one_chunk", 1), ("four_chunks", 4)):
@@ -412,16 +413,18 @@ def _mixed_case(msgl, dev, n_chunks, iters):
     out_dec, out_ext = torch.empty_like(q_dec), torch.empty_like(q_ext)
     ws_dec = torch.zeros(max(msgl.paged_decode_workspace_size(64, 32, 128, p.max_len, 16), 256),
                          dtype=torch.uint8, device=dev)
+    ws_ext = torch.empty(max(msgl.paged_extend_workspace_size(p.pool, 512 * n_chunks, p.max_len, 32),
+                             256), dtype=torch.uint8, device=dev)
 
     def mixed():
         msgl.paged_mixed(p.pool, wl.layer, p.q, p.pt, p.ti, p.pl, p.el, p.cu, p.max_ext, p.max_len,
                          out=out, workspace=p.ws)
 
-    def separate():
+    def separate(split=True):
         msgl.paged_decode(p.pool, wl.layer, q_dec, p.pt, ti_dec, sl_dec, p.max_len, out=out_dec,
                           workspace=ws_dec)
         msgl.paged_extend(p.pool, wl.layer, q_ext, p.pt, ti_ext, pl_ext, el_ext, cu_ext, 512,
-                          p.max_len, out=out_ext)
+                          p.max_len, out=out_ext, workspace=ws_ext, split=split)
 
     def mixed_split():
         os.environ["MSGL_MIXED_SPLIT"] = "1"
@@ -432,6 +435,7 @@ def _mixed_case(msgl, dev, n_chunks, iters):
 
     res = {"decode_rows": 64, "extend_rows": n_chunks, "extend_tokens": 512 * n_chunks}
     for name, fn in (("mixed_call_us", mixed), ("separate_calls_us", separate),
+                     ("separate_calls_unsplit_us", lambda: separate(False)),
                      ("mixed_split_launches_us", mixed_split)):
         for _ in range(3):
             fn()
